@@ -1,0 +1,213 @@
+"""Python binding of libcpattn (ctypes): argument marshalling only.
+
+Each function has the name of the C entry point it calls and performs no
+computation of its own: tensors are turned into (pointer, strides), the
+current torch stream is passed along, and a non-zero status raises
+``CpattnError`` with the library's message. There is no fallback path: if the
+shared library is missing, every call raises.
+
+Tensor layouts (torch tensors on the GPU):
+  q, k, v, dout          [B, H, T, D]  bf16 or fp32, last dimension contiguous
+  o, dq/dk/dv accum.     [B, H, T, D]  fp32
+  lse, delta             [B, H, T]     fp32
+A position map is a 4-tuple (len, split, d0, d1): local index i sits at global
+position i + (d0 if i < split else d1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+__all__ = [
+    "CpattnError", "lib_path", "load", "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard",
+    "cpattn_rope_table", "cpattn_block_fwd", "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes",
+    "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "EXPORTS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libcpattn.so")
+
+CPATTN_F32, CPATTN_BF16 = 0, 1
+
+EXPORTS = (
+    "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
+    "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
+    "cpattn_block_bwd",
+)
+
+
+class CpattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libcpattn error {code}: {msg}")
+        self.code = code
+
+
+class cpattn_posmap(ctypes.Structure):
+    _fields_ = [("len", ctypes.c_int64), ("split", ctypes.c_int64), ("d0", ctypes.c_int64), ("d1", ctypes.c_int64)]
+
+
+class cpattn_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64), ("st", ctypes.c_int64)]
+
+
+_P = ctypes.POINTER
+_i32, _i64, _f32, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+_T, _M = _P(cpattn_tensor), _P(cpattn_posmap)
+
+_SIGS = {
+    "cpattn_version": (ctypes.c_int, []),
+    "cpattn_last_error": (ctypes.c_char_p, []),
+    "cpattn_headtail_shard": (ctypes.c_int, [_i64, _i32, _i32, _M, _P(_i32)]),
+    "cpattn_rope_table": (ctypes.c_int, [_f64, _i64, _i64, _vp, _vp]),
+    "cpattn_block_fwd": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32, _f32, _vp,
+                                        _i64, _i64, _i64, _T, _T, _vp]),
+    "cpattn_lse_merge": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
+                                       _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
+    "cpattn_bwd_preprocess": (ctypes.c_int, [_T, _i32, _T, _T, _i64, _i64, _i64, _i64, _vp]),
+    "cpattn_block_bwd": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M,
+                                        _M, _i32, _f32, _vp]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libcpattn.so (built in-tree by build.py); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise CpattnError(-100, f"{lib_path} is missing: build it with context_causal_attention_cpattn_amd/build.py")
+        lib = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise CpattnError(status, load().cpattn_last_error().decode())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _tensor(t, ndim: int = 4) -> cpattn_tensor:
+    if t.dim() != ndim:
+        raise ValueError(f"expected a {ndim}-D tensor, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError("libcpattn takes GPU tensors")
+    if ndim == 4 and t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError("the last dimension must be contiguous")
+    s = t.stride()
+    return cpattn_tensor(t.data_ptr(), s[0], s[1], s[2])
+
+
+def _map(m) -> cpattn_posmap:
+    if isinstance(m, cpattn_posmap):
+        return m
+    return cpattn_posmap(*[int(x) for x in m])
+
+
+def _dtype(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return CPATTN_BF16
+    if t.dtype == torch.float32:
+        return CPATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def cpattn_version() -> int:
+    return load().cpattn_version()
+
+
+def cpattn_last_error() -> str:
+    return load().cpattn_last_error().decode()
+
+
+def cpattn_headtail_shard(T: int, ring: int, rank: int):
+    """Return ((len, split, d0, d1), positions) of rank ``rank`` (host call)."""
+    m = cpattn_posmap()
+    n = T // (2 * ring) * 2 if ring > 0 and T > 0 else 0
+    pos = (ctypes.c_int32 * max(n, 1))()
+    _check(load().cpattn_headtail_shard(T, ring, rank, ctypes.byref(m), pos))
+    return (m.len, m.split, m.d0, m.d1), list(pos[: m.len])
+
+
+def cpattn_rope_table(theta: float, rows: int, D: int, table, stream=None):
+    """Fill ``table`` (fp32 GPU tensor of rows*D elements) with (cos, sin) pairs."""
+    if table.numel() < rows * D or not table.is_contiguous():
+        raise ValueError("table must be a contiguous fp32 tensor of rows*D elements")
+    _check(load().cpattn_rope_table(float(theta), rows, D, ctypes.c_void_p(table.data_ptr()), _stream(stream)))
+
+
+def _rope_args(rope_table):
+    if rope_table is None:
+        return None, 0
+    return ctypes.c_void_p(rope_table.data_ptr()), rope_table.shape[0]
+
+
+def cpattn_block_fwd(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: float = 0.0, rope_table=None,
+                     row_begin: int = 0, row_end: int | None = None, stream=None):
+    """O, LSE of rows [row_begin, row_end) of q against one KV block (rope_table: [rows, D] fp32)."""
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    rp, rr = _rope_args(rope_table)
+    _check(load().cpattn_block_fwd(
+        _tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, Tq, Tk, D, _map(qmap), _map(kmap), int(causal),
+        float(scale), rp, rr, row_begin, Tq if row_end is None else row_end, _tensor(o), _tensor(lse, 3),
+        _stream(stream)))
+
+
+def cpattn_lse_merge(o_acc, lse_acc, o_blk, lse_blk, row_begin: int = 0, row_end: int | None = None, stream=None):
+    B, H, T, D = o_acc.shape
+    _check(load().cpattn_lse_merge(_tensor(o_acc), _tensor(lse_acc, 3), _tensor(o_blk), _tensor(lse_blk, 3), B, H, T,
+                                   D, row_begin, T if row_end is None else row_end, _stream(stream)))
+
+
+def cpattn_ring_fwd_workspace_bytes(B: int, H: int, Tq: int, D: int) -> int:
+    return int(load().cpattn_ring_fwd_workspace_bytes(B, H, Tq, D))
+
+
+def cpattn_ring_fwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, o_acc, lse_acc,
+                    workspace, causal: bool = True, scale: float = 0.0, rope_table=None, stream=None):
+    """Ring forward of rank ``rank``; k_blocks[i]/v_blocks[i]/kmaps[i] belong to rank i."""
+    n = len(k_blocks)
+    if len(v_blocks) != n or len(kmaps) != n:
+        raise ValueError("k_blocks, v_blocks, kmaps must have the same length")
+    B, H, Tq, D = q.shape
+    Tk = k_blocks[0].shape[2]
+    ks = (cpattn_tensor * n)(*[_tensor(t) for t in k_blocks])
+    vs = (cpattn_tensor * n)(*[_tensor(t) for t in v_blocks])
+    ms = (cpattn_posmap * n)(*[_map(m) for m in kmaps])
+    rp, rr = _rope_args(rope_table)
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().cpattn_ring_fwd(_tensor(q), ks, vs, ms, n, rank, _map(qmap), _dtype(q), B, H, Tq, Tk, D,
+                                  int(causal), float(scale), rp, rr, _tensor(o_acc), _tensor(lse_acc, 3), ws, wsb,
+                                  _stream(stream)))
+
+
+def cpattn_bwd_preprocess(dout, o, delta, stream=None):
+    B, H, Tq, D = dout.shape
+    _check(load().cpattn_bwd_preprocess(_tensor(dout), _dtype(dout), _tensor(o), _tensor(delta, 3), B, H, Tq, D,
+                                        _stream(stream)))
+
+
+def cpattn_block_bwd(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
+                     scale: float = 0.0, stream=None):
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    _check(load().cpattn_block_bwd(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
+                                   _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq, Tk,
+                                   D, _map(qmap), _map(kmap), int(causal), float(scale), _stream(stream)))

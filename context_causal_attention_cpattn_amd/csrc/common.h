@@ -1,0 +1,71 @@
+// Shared device-side definitions for the libcpattn kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Local index -> global position: i + (i < split ? d0 : d1), d1 >= d0.
+struct PosMap {
+  int len, split, d0, d1;
+  __device__ __host__ __forceinline__ int pos(int i) const { return i + (i < split ? d0 : d1); }
+  // number of local indices whose position is < P (positions increase with i)
+  __device__ __host__ __forceinline__ int count_lt(int P) const {
+    int a = P - d0;
+    a = a < 0 ? 0 : (a > split ? split : a);
+    int b = P - d1 - split;
+    int tail = len - split;
+    b = b < 0 ? 0 : (b > tail ? tail : b);
+    return a + b;
+  }
+  __device__ __host__ __forceinline__ int count_le(int P) const { return count_lt(P + 1); }
+};
+
+// One v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] B[16x32].
+// Lane l supplies A row (l % 32), B column (l % 32), 8 consecutive k values
+// each; the accumulator holds column (l % 32), rows 8*(r/4) + 4*(l/32) + r%4.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of a 4-row x 16-column block of 16-bit values.
+// Within every group of 16 lanes, output lane i element e is element (i % 4)
+// of the 8 bytes addressed by source lane 4*e + i/4. To give lane i the
+// column i of rows r0..r0+3 of a row-major tile, source lane s must address
+// row r0 + (s % 16) / 4, column c0 + 4 * (s % 4).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+  r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup id -> logical tile id so that consecutive logical tiles land on
+// the same XCD. Workgroups are dealt to the 8 XCDs round-robin by id, so XCD x
+// runs ids x, x+8, x+16, ...; logical tiles [x*per + min(x,rem), ...) go there.
+__device__ __forceinline__ int xcd_remap(int wg, int n) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = wg & 7, slot = wg >> 3;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+}  // namespace cpattn

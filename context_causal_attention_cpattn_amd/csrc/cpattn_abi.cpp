@@ -1,0 +1,318 @@
+// C ABI of libcpattn: argument validation, the HeadTail shard map, the ring
+// driver and dispatch to the HIP kernels. No exception crosses the boundary;
+// every error is a status code plus a thread-local message.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/cpattn.h"
+#include "internal.h"
+
+using namespace cpattn;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return CPATTN_OK;
+}
+
+constexpr int64_t kIntMax = 2147483647;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A [B,H,T,D] tensor of `esize`-byte elements: non-null, 16-byte aligned,
+// strides that keep every row 16-byte aligned.
+int check_tensor(const cpattn_tensor* t, const char* name, int esize) {
+  if (!t || !t->data) return fail(CPATTN_EINVAL, "%s: null tensor", name);
+  if (!aligned16(t->data)) return fail(CPATTN_EINVAL, "%s: pointer not 16-byte aligned", name);
+  const int64_t q = 16 / esize;
+  if (t->sb % q || t->sh % q || t->st % q)
+    return fail(CPATTN_EINVAL, "%s: B/H/T strides must be multiples of %lld elements", name, (long long)q);
+  if (t->sb < 0 || t->sh < 0 || t->st < 0) return fail(CPATTN_EINVAL, "%s: negative stride", name);
+  return CPATTN_OK;
+}
+
+int check_rows(const cpattn_tensor* t, const char* name) {  // [B,H,T] fp32
+  if (!t || !t->data) return fail(CPATTN_EINVAL, "%s: null tensor", name);
+  if (((uintptr_t)t->data & 3u) != 0) return fail(CPATTN_EINVAL, "%s: pointer not 4-byte aligned", name);
+  if (t->sb < 0 || t->sh < 0 || t->st < 0) return fail(CPATTN_EINVAL, "%s: negative stride", name);
+  return CPATTN_OK;
+}
+
+int check_map(const cpattn_posmap* m, int64_t len, const char* name) {
+  if (!m) return fail(CPATTN_EINVAL, "%s: null map", name);
+  if (m->len != len) return fail(CPATTN_EINVAL, "%s: len %lld != %lld", name, (long long)m->len, (long long)len);
+  if (m->split < 0 || m->split > m->len) return fail(CPATTN_EINVAL, "%s: split outside [0, len]", name);
+  if (m->d1 < m->d0) return fail(CPATTN_EINVAL, "%s: d1 < d0 (positions must increase)", name);
+  if (m->d0 < 0) return fail(CPATTN_EINVAL, "%s: negative position", name);
+  if (m->len + m->d1 >= kIntMax) return fail(CPATTN_EINVAL, "%s: positions exceed 2^31", name);
+  return CPATTN_OK;
+}
+
+PosMap to_map(const cpattn_posmap* m) {
+  return PosMap{(int)m->len, (int)m->split, (int)m->d0, (int)m->d1};
+}
+
+View view(const cpattn_tensor* t) { return View{t->data, t->sb, t->sh, t->st}; }
+
+// Largest global position in the map (the last index; positions increase).
+int64_t max_pos(const cpattn_posmap* m) {
+  if (m->len <= 0) return -1;
+  const int64_t i = m->len - 1;
+  return i + (i < m->split ? m->d0 : m->d1);
+}
+
+int check_dims(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D) {
+  if (B <= 0 || H <= 0 || Tq <= 0 || Tk <= 0 || D <= 0)
+    return fail(CPATTN_EINVAL, "B, H, Tq, Tk, D must be positive");
+  if (B * H > kIntMax || Tq > kIntMax || Tk > kIntMax) return fail(CPATTN_EINVAL, "sizes exceed 2^31");
+  if (D != 64 && D != 128) return fail(CPATTN_EUNSUPPORTED, "D = %lld (supported: 64, 128)", (long long)D);
+  return CPATTN_OK;
+}
+
+int build_fwd(FwdArgs& a, const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
+              int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+              const cpattn_posmap* kmap, int32_t causal, float scale, const float* rope, int64_t rope_rows,
+              int64_t row_begin, int64_t row_end, const cpattn_tensor* o, const cpattn_tensor* lse) {
+  int st;
+  if ((st = check_dims(B, H, Tq, Tk, D))) return st;
+  if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d", (int)dtype);
+  const int es = dtype == CPATTN_BF16 ? 2 : 4;
+  if ((st = check_tensor(q, "q", es)) || (st = check_tensor(k, "k", es)) || (st = check_tensor(v, "v", es)) ||
+      (st = check_tensor(o, "o", 4)) || (st = check_rows(lse, "lse")))
+    return st;
+  if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
+  if (row_begin < 0 || row_end > Tq || row_begin >= row_end)
+    return fail(CPATTN_EINVAL, "row range [%lld, %lld) outside [0, %lld) or empty", (long long)row_begin,
+                (long long)row_end, (long long)Tq);
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
+  if (rope) {
+    if (dtype != CPATTN_BF16) return fail(CPATTN_EUNSUPPORTED, "rotary table with fp32 inputs");
+    if (((uintptr_t)rope & 15u) != 0) return fail(CPATTN_EINVAL, "rope table not 16-byte aligned");
+    if (rope_rows <= 0 || rope_rows > kIntMax) return fail(CPATTN_EINVAL, "rope_rows");
+    if (max_pos(qmap) >= rope_rows || max_pos(kmap) >= rope_rows)
+      return fail(CPATTN_EINVAL, "a global position is outside the rotary table (%lld rows)", (long long)rope_rows);
+  }
+  a.q = view(q);
+  a.k = view(k);
+  a.v = view(v);
+  a.o = (float*)o->data;
+  a.o_sb = o->sb, a.o_sh = o->sh, a.o_st = o->st;
+  a.lse = (float*)lse->data;
+  a.l_sb = lse->sb, a.l_sh = lse->sh, a.l_st = lse->st;
+  a.B = (int)B, a.H = (int)H, a.Tq = (int)Tq, a.Tk = (int)Tk, a.D = (int)D;
+  a.qm = to_map(qmap);
+  a.km = to_map(kmap);
+  a.causal = causal != 0;
+  a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  a.rope = rope;
+  a.rope_rows = (int)rope_rows;
+  a.row_begin = (int)row_begin;
+  a.row_end = (int)row_end;
+  return CPATTN_OK;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CPATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpattn_version(void) { return CPATTN_ABI_VERSION; }
+
+const char* cpattn_last_error(void) { return g_err; }
+
+int cpattn_headtail_shard(int64_t T, int32_t ring, int32_t rank, cpattn_posmap* map, int32_t* positions) {
+  if (!map) return fail(CPATTN_EINVAL, "map is NULL");
+  if (T <= 0 || ring <= 0) return fail(CPATTN_EINVAL, "T and ring must be positive");
+  if (T >= kIntMax) return fail(CPATTN_EINVAL, "T must be below 2^31");
+  if (T % (2 * (int64_t)ring) != 0) return fail(CPATTN_EINVAL, "T %% (2*ring) != 0");
+  if (rank < 0 || rank >= ring) return fail(CPATTN_EINVAL, "rank outside [0, ring)");
+  const int64_t c = T / (2 * (int64_t)ring);
+  map->len = 2 * c;
+  map->split = c;
+  map->d0 = (int64_t)rank * c;                       // head chunk `rank`
+  map->d1 = (int64_t)(2 * ring - 1 - rank) * c - c;  // tail chunk 2*ring-1-rank, local index starts at c
+  if (positions)
+    for (int64_t i = 0; i < 2 * c; ++i) positions[i] = (int32_t)(i + (i < c ? map->d0 : map->d1));
+  return ok();
+}
+
+int cpattn_rope_table(double theta, int64_t rows, int64_t D, float* table, void* stream) {
+  if (!(theta > 0.0) || std::isinf(theta)) return fail(CPATTN_EINVAL, "theta must be positive");
+  if (rows <= 0 || rows > kIntMax || D <= 0 || D % 2 || D > 4096) return fail(CPATTN_EINVAL, "rows / D");
+  if (!table) return fail(CPATTN_EINVAL, "table is NULL");
+  return launch_status(launch_rope_table(theta, (int)rows, (int)D, table, (hipStream_t)stream), "rope_table");
+}
+
+int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
+                     int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+                     const cpattn_posmap* kmap, int32_t causal, float scale, const float* rope_table,
+                     int64_t rope_rows, int64_t row_begin, int64_t row_end, const cpattn_tensor* o,
+                     const cpattn_tensor* lse, void* stream) {
+  FwdArgs a{};
+  int st = build_fwd(a, q, k, v, dtype, B, H, Tq, Tk, D, qmap, kmap, causal, scale, rope_table, rope_rows,
+                     row_begin, row_end, o, lse);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_status(dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s), "block_fwd");
+}
+
+int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, const cpattn_tensor* o_blk,
+                     const cpattn_tensor* lse_blk, int64_t B, int64_t H, int64_t T, int64_t D, int64_t row_begin,
+                     int64_t row_end, void* stream) {
+  int st;
+  if (B <= 0 || H <= 0 || T <= 0 || D <= 0) return fail(CPATTN_EINVAL, "B, H, T, D must be positive");
+  if (B * H > kIntMax || T > kIntMax) return fail(CPATTN_EINVAL, "sizes exceed 2^31");
+  if (D != 64 && D != 128) return fail(CPATTN_EUNSUPPORTED, "D = %lld (supported: 64, 128)", (long long)D);
+  if ((st = check_tensor(o_acc, "o_acc", 4)) || (st = check_tensor(o_blk, "o_blk", 4)) ||
+      (st = check_rows(lse_acc, "lse_acc")) || (st = check_rows(lse_blk, "lse_blk")))
+    return st;
+  if (row_begin < 0 || row_end > T || row_begin >= row_end) return fail(CPATTN_EINVAL, "row range");
+  MergeArgs m{};
+  m.o_acc = (float*)o_acc->data, m.oa_sb = o_acc->sb, m.oa_sh = o_acc->sh, m.oa_st = o_acc->st;
+  m.l_acc = (float*)lse_acc->data, m.la_sb = lse_acc->sb, m.la_sh = lse_acc->sh, m.la_st = lse_acc->st;
+  m.o_blk = (const float*)o_blk->data, m.ob_sb = o_blk->sb, m.ob_sh = o_blk->sh, m.ob_st = o_blk->st;
+  m.l_blk = (const float*)lse_blk->data, m.lb_sb = lse_blk->sb, m.lb_sh = lse_blk->sh, m.lb_st = lse_blk->st;
+  m.B = (int)B, m.H = (int)H, m.D = (int)D;
+  m.row_begin = (int)row_begin, m.row_end = (int)row_end;
+  return launch_status(launch_merge(m, (hipStream_t)stream), "lse_merge");
+}
+
+size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D) {
+  if (B <= 0 || H <= 0 || Tq <= 0 || D <= 0) return 0;
+  const size_t o = (size_t)B * H * Tq * D * 4;
+  const size_t l = (size_t)B * H * Tq * 4;
+  return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+}
+
+int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const cpattn_tensor* v_blocks,
+                    const cpattn_posmap* kmaps, int32_t ring, int32_t rank, const cpattn_posmap* qmap,
+                    int32_t dtype, int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t causal,
+                    float scale, const float* rope_table, int64_t rope_rows, const cpattn_tensor* o_acc,
+                    const cpattn_tensor* lse_acc, void* workspace, size_t workspace_bytes, void* stream) {
+  if (ring < 1) return fail(CPATTN_EINVAL, "ring must be >= 1");
+  if (rank < 0 || rank >= ring) return fail(CPATTN_EINVAL, "rank outside [0, ring)");
+  if (!k_blocks || !v_blocks || !kmaps) return fail(CPATTN_EINVAL, "null block arrays");
+  // validate every step before launching anything
+  int st;
+  for (int32_t i = 0; i < ring; ++i) {
+    FwdArgs a{};
+    if ((st = build_fwd(a, q, &k_blocks[i], &v_blocks[i], dtype, B, H, Tq, Tk, D, qmap, &kmaps[i], causal, scale,
+                        rope_table, rope_rows, 0, Tq, o_acc, lse_acc)))
+      return st;
+  }
+  const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Tq, D);
+  if (ring > 1) {
+    if (!workspace || workspace_bytes < need)
+      return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");
+  }
+  float* o_ws = (float*)workspace;
+  float* l_ws = (float*)((char*)workspace + ((size_t)B * H * Tq * D * 4 + 255) / 256 * 256);
+  cpattn_tensor o_blk{o_ws, H * Tq * D, Tq * D, D};
+  cpattn_tensor l_blk{l_ws, H * Tq, Tq, 1};
+  hipStream_t s = (hipStream_t)stream;
+  const PosMap qm = to_map(qmap);
+  for (int32_t step = 0; step < ring; ++step) {
+    const int32_t src = ((rank - step) % ring + ring) % ring;
+    const cpattn_posmap* km = &kmaps[src];
+    // rows that see at least one key of this block: positions >= the block's first key
+    int64_t rb = 0;
+    if (causal) {
+      const int64_t first_key_pos = km->len > 0 ? (km->split > 0 ? km->d0 : km->d1) : 0;
+      rb = qm.count_lt((int)first_key_pos);
+    }
+    if (step == 0) {
+      // step 0 fills every row of the accumulator (rows without a visible key get O = 0, LSE = -inf)
+      FwdArgs a{};
+      build_fwd(a, q, &k_blocks[src], &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, rope_table,
+                rope_rows, 0, Tq, o_acc, lse_acc);
+      hipError_t e = dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
+      if (e != hipSuccess) return launch_status(e, "ring_fwd step 0");
+      continue;
+    }
+    if (rb >= Tq) continue;  // the whole block is in the future of every local row
+    FwdArgs a{};
+    build_fwd(a, q, &k_blocks[src], &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, rope_table,
+              rope_rows, rb, Tq, &o_blk, &l_blk);
+    hipError_t e = dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
+    if (e != hipSuccess) return launch_status(e, "ring_fwd block");
+    MergeArgs m{};
+    m.o_acc = (float*)o_acc->data, m.oa_sb = o_acc->sb, m.oa_sh = o_acc->sh, m.oa_st = o_acc->st;
+    m.l_acc = (float*)lse_acc->data, m.la_sb = lse_acc->sb, m.la_sh = lse_acc->sh, m.la_st = lse_acc->st;
+    m.o_blk = o_ws, m.ob_sb = o_blk.sb, m.ob_sh = o_blk.sh, m.ob_st = o_blk.st;
+    m.l_blk = l_ws, m.lb_sb = l_blk.sb, m.lb_sh = l_blk.sh, m.lb_st = l_blk.st;
+    m.B = (int)B, m.H = (int)H, m.D = (int)D;
+    m.row_begin = (int)rb, m.row_end = (int)Tq;
+    e = launch_merge(m, s);
+    if (e != hipSuccess) return launch_status(e, "ring_fwd merge");
+  }
+  return ok();
+}
+
+int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* o,
+                          const cpattn_tensor* delta, int64_t B, int64_t H, int64_t Tq, int64_t D, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Tq, 1, D))) return st;
+  if (dtype != CPATTN_F32 && dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d", (int)dtype);
+  if ((st = check_tensor(dout, "dout", dtype == CPATTN_BF16 ? 2 : 4)) || (st = check_tensor(o, "o", 4)) ||
+      (st = check_rows(delta, "delta")))
+    return st;
+  PreArgs p{};
+  p.dout = view(dout);
+  p.bf16 = dtype == CPATTN_BF16;
+  p.o = view(o);
+  p.delta = (float*)delta->data, p.d_sb = delta->sb, p.d_sh = delta->sh, p.d_st = delta->st;
+  p.B = (int)B, p.H = (int)H, p.Tq = (int)Tq, p.D = (int)D;
+  return launch_status(launch_bwd_preprocess(p, (hipStream_t)stream), "bwd_preprocess");
+}
+
+int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                     const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
+                     const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
+                     int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+                     const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, Tq, Tk, D))) return st;
+  if (dtype == CPATTN_F32) return fail(CPATTN_EUNSUPPORTED, "block backward takes bf16 inputs");
+  if (dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d", (int)dtype);
+  if ((st = check_tensor(q, "q", 2)) || (st = check_tensor(k, "k", 2)) || (st = check_tensor(v, "v", 2)) ||
+      (st = check_tensor(dout, "dout", 2)) || (st = check_rows(lse, "lse")) || (st = check_rows(delta, "delta")) ||
+      (st = check_tensor(dq_acc, "dq_acc", 4)) || (st = check_tensor(dk_acc, "dk_acc", 4)) ||
+      (st = check_tensor(dv_acc, "dv_acc", 4)))
+    return st;
+  if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
+  BwdArgs a{};
+  a.q = view(q), a.k = view(k), a.v = view(v), a.dout = view(dout);
+  a.lse = view(lse), a.delta = view(delta);
+  a.dq = (float*)dq_acc->data, a.dq_sb = dq_acc->sb, a.dq_sh = dq_acc->sh, a.dq_st = dq_acc->st;
+  a.dk = (float*)dk_acc->data, a.dk_sb = dk_acc->sb, a.dk_sh = dk_acc->sh, a.dk_st = dk_acc->st;
+  a.dv = (float*)dv_acc->data, a.dv_sb = dv_acc->sb, a.dv_sh = dv_acc->sh, a.dv_st = dv_acc->st;
+  a.B = (int)B, a.H = (int)H, a.Tq = (int)Tq, a.Tk = (int)Tk, a.D = (int)D;
+  a.qm = to_map(qmap), a.km = to_map(kmap);
+  a.causal = causal != 0;
+  a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  return launch_status(launch_bwd_bf16(a, (hipStream_t)stream), "block_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Host-side launch interface between the C ABI (cpattn_abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace cpattn {
+
+struct View {  // [B,H,T,D] (or [B,H,T]) view; D stride 1
+  const void* p;
+  int64_t sb, sh, st;
+};
+
+struct FwdArgs {
+  View q, k, v;
+  float* o;
+  int64_t o_sb, o_sh, o_st;
+  float* lse;
+  int64_t l_sb, l_sh, l_st;
+  int B, H, Tq, Tk, D;
+  PosMap qm, km;
+  int causal;
+  float scale;
+  const float* rope;  // [rope_rows][D/2][2] or null
+  int rope_rows;
+  int row_begin, row_end;
+};
+
+struct MergeArgs {
+  float* o_acc;
+  int64_t oa_sb, oa_sh, oa_st;
+  float* l_acc;
+  int64_t la_sb, la_sh, la_st;
+  const float* o_blk;
+  int64_t ob_sb, ob_sh, ob_st;
+  const float* l_blk;
+  int64_t lb_sb, lb_sh, lb_st;
+  int B, H, D;
+  int row_begin, row_end;
+};
+
+struct PreArgs {
+  View dout;
+  int bf16;
+  View o;
+  float* delta;
+  int64_t d_sb, d_sh, d_st;
+  int B, H, Tq, D;
+};
+
+struct BwdArgs {
+  View q, k, v, dout;
+  View lse, delta;
+  float* dq;
+  int64_t dq_sb, dq_sh, dq_st;
+  float* dk;
+  int64_t dk_sb, dk_sh, dk_st;
+  float* dv;
+  int64_t dv_sb, dv_sh, dv_st;
+  int B, H, Tq, Tk, D;
+  PosMap qm, km;
+  int causal;
+  float scale;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_bwd_preprocess(const PreArgs& a, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStream_t s);
+
+}  // namespace cpattn

@@ -1,0 +1,155 @@
+// Bandwidth-bound kernels: the log-sum-exp merge (SDPAMerger) and the
+// backward row term delta = rowsum(dO * O).
+//
+// Merge (BluScriptCP development log, 2026-03-20 SDPAMerger; 2026-05-20 merge
+// of a row range): for every row of the range
+//   M = max(L_acc, L_blk), L = M + log(exp(L_acc - M) + exp(L_blk - M)),
+//   O = exp(L_acc - L) O_acc + exp(L_blk - L) O_blk,  in place into (O_acc, L_acc).
+// Each thread owns 16-byte slices of rows; a row's two LSE values are read by
+// all lanes that share the row (one cache line per wave). Bytes per row:
+// 3 * 4D (two O reads, one O write) + 12 (two LSE reads, one write).
+
+#include "internal.h"
+
+namespace cpattn {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_vec) {
+  constexpr int VPR = D / 4;  // float4 per row
+  const int rows = a.row_end - a.row_begin;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
+    const int64_t rr = i / VPR;
+    const int c = (int)(i - rr * VPR) * 4;
+    const int64_t bh = rr / rows;
+    const int row = a.row_begin + (int)(rr - bh * rows);
+    const int b = (int)(bh / a.H), hh = (int)(bh - (int64_t)b * a.H);
+    float* la = a.l_acc + b * a.la_sb + hh * a.la_sh + (int64_t)row * a.la_st;
+    const float lb = a.l_blk[b * a.lb_sb + hh * a.lb_sh + (int64_t)row * a.lb_st];
+    const float lav = *la;
+    float* oa = a.o_acc + b * a.oa_sb + hh * a.oa_sh + (int64_t)row * a.oa_st + c;
+    const float* ob = a.o_blk + b * a.ob_sb + hh * a.ob_sh + (int64_t)row * a.ob_st + c;
+    const f32x4 xa = *(const f32x4*)oa;
+    const f32x4 xb = __builtin_nontemporal_load((const f32x4*)ob);
+    const float m = fmaxf(lav, lb);
+    f32x4 y;
+    float lnew;
+    if (m == -INFINITY) {
+      y = f32x4{0.f, 0.f, 0.f, 0.f};
+      lnew = -INFINITY;
+    } else {
+      const float ea = expf(lav - m), eb = expf(lb - m);  // exp(-inf) = 0
+      const float tot = ea + eb;
+      const float inv = 1.f / tot;
+      const float wa = ea * inv, wb = eb * inv;
+      y = wa * xa + wb * xb;
+      lnew = m + logf(tot);
+    }
+    *(f32x4*)oa = y;
+    if (c == 0) *la = lnew;
+  }
+}
+
+template <int D>
+hipError_t merge_d(const MergeArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.H * (a.row_end - a.row_begin);
+  const int64_t n_vec = rows * (D / 4);
+  if (n_vec <= 0) return hipSuccess;
+  int64_t blocks = (n_vec + 255) / 256;
+  const int64_t cap = 256 * 64;  // 64 workgroups per CU at most; the loop covers the rest
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, a, n_vec);
+  return hipGetLastError();
+}
+
+// delta[row] = sum_d dout[row][d] * o[row][d]; 16 lanes per row, 8 elements each (D = 128)
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void delta_kernel(PreArgs a, int64_t n_rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t rr = gid / LPR;
+  const int c = (int)(gid % LPR) * 8;
+  float sum = 0.f;
+  int b = 0, hh = 0, t = 0;
+  if (rr < n_rows) {
+    const int64_t bh = rr / a.Tq;
+    t = (int)(rr - bh * a.Tq);
+    b = (int)(bh / a.H);
+    hh = (int)(bh - (int64_t)b * a.H);
+    const float* op = (const float*)a.o.p + b * a.o.sb + hh * a.o.sh + (int64_t)t * a.o.st + c;
+    const f32x4 o0 = *(const f32x4*)op, o1 = *(const f32x4*)(op + 4);
+    float g[8];
+    if constexpr (BF16) {
+      const __bf16* dp = (const __bf16*)a.dout.p + b * a.dout.sb + hh * a.dout.sh + (int64_t)t * a.dout.st + c;
+      const bf16x8 x = *(const bf16x8*)dp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = (float)x[e];
+    } else {
+      const float* dp = (const float*)a.dout.p + b * a.dout.sb + hh * a.dout.sh + (int64_t)t * a.dout.st + c;
+      const f32x4 x0 = *(const f32x4*)dp, x1 = *(const f32x4*)(dp + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { g[e] = x0[e]; g[e + 4] = x1[e]; }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum = fmaf(g[e], o0[e], sum);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum = fmaf(g[e + 4], o1[e], sum);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (rr < n_rows && c == 0) a.delta[b * a.d_sb + hh * a.d_sh + (int64_t)t * a.d_st] = sum;
+}
+
+template <int D>
+hipError_t delta_d(const PreArgs& a, hipStream_t s) {
+  const int64_t n_rows = (int64_t)a.B * a.H * a.Tq;
+  const int64_t threads = n_rows * (D / 8);
+  if (threads <= 0) return hipSuccess;
+  const int64_t blocks = (threads + 255) / 256;
+  if (a.bf16)
+    hipLaunchKernelGGL((delta_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a, n_rows);
+  else
+    hipLaunchKernelGGL((delta_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a, n_rows);
+  return hipGetLastError();
+}
+
+// Rotary table: table[p][i] = (cos, sin)(p * theta^(-2i/D)); angle and reduction in fp64.
+__global__ void rope_table_kernel(double theta, int rows, int D, float* table) {
+  const int64_t n = (int64_t)rows * (D / 2);
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n; g += (int64_t)gridDim.x * blockDim.x) {
+    const int p = (int)(g / (D / 2)), i = (int)(g % (D / 2));
+    const double inv = pow(theta, -2.0 * (double)i / (double)D);
+    const double ang = (double)p * inv;
+    table[2 * g] = (float)cos(ang);
+    table[2 * g + 1] = (float)sin(ang);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 64: return merge_d<64>(a, s);
+    case 128: return merge_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_preprocess(const PreArgs& a, hipStream_t s) {
+  switch (a.D) {
+    case 64: return delta_d<64>(a, s);
+    case 128: return delta_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStream_t s) {
+  const int64_t n = (int64_t)rows * (D / 2);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s, theta, rows, D, table);
+  return hipGetLastError();
+}
+
+}  // namespace cpattn

@@ -1,0 +1,206 @@
+/*
+ * libcpattn -- one rank's share of causal ring attention under HeadTail
+ * load-balanced context parallelism, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the pages on context parallelism (BluScriptCP
+ * development log, docs/Claude Logs.md):
+ *   - HeadTail shard map: entries of 2026-05-16 (chunk-level HeadTail) and
+ *     2026-06-29 / 2026-07-10 (RopeDeltas.h: local index -> global position
+ *     through a head delta and a tail delta);
+ *   - block attention with separate query/key lengths, global positions for
+ *     the causal mask, and the log-sum-exp as an output: entries of
+ *     2026-04-20 and 2026-06-29 (kernel requirements);
+ *   - the SDPAMerger log-sum-exp merge: entries of 2026-03-20 and 2026-05-20
+ *     (merge of a row range);
+ *   - the ring forward: entry of 2026-03-20 (ring rotator, per-step SDPA,
+ *     merger); the per-block backward with gradients accumulated across ring
+ *     steps: entries of 2026-04-20 and 2026-05-07;
+ *   - strided Q/K/V/dO/O/LSE/dQ/dK/dV: entry of 2026-04-28;
+ *   - rotary embedding at global positions: entries of 2026-06-29 and
+ *     2026-07-10.
+ *
+ * Conventions shared by every call
+ *   - Tensors are described by cpattn_tensor: a pointer to element [0,0,0,0]
+ *     and element strides for the B, H and T dimensions. The D dimension is
+ *     contiguous (stride 1). LSE/delta arrays are [B,H,T] and use sb, sh, st.
+ *     Pointers must be aligned to 16 bytes and the B/H/T strides of bf16
+ *     tensors must be multiples of 8 elements (of fp32 tensors, multiples of 4).
+ *   - Device pointers are HIP device memory owned by the caller. The library
+ *     allocates nothing, keeps no device state and never synchronises: every
+ *     kernel is launched on the hipStream_t passed as `stream` (NULL = the
+ *     default stream). Host arrays are read during the call only.
+ *   - Global positions: a cpattn_posmap maps local index i in [0, len) to
+ *     global position i + (i < split ? d0 : d1), with 0 <= split <= len and
+ *     d1 >= d0 (positions increase with the local index). A contiguous shard
+ *     is split = len, d0 = first global position.
+ *   - Causal visibility: key j is visible from query p iff
+ *     pos_k(j) <= pos_q(p) (self included). causal = 0 makes every key visible.
+ *   - The softmax scale is `scale`; pass 0 for 1/sqrt(D).
+ *   - LSE is the natural-log log-sum-exp of the scaled scores of the visible
+ *     keys. A row with no visible key gets O = 0 and LSE = -inf.
+ *   - Return value: CPATTN_OK, or a negative code; cpattn_last_error() then
+ *     returns a message (thread-local). Arguments are validated before any
+ *     launch; on error nothing is launched. Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Stateless and thread-safe; concurrent calls on different streams must
+ *     not write the same memory.
+ */
+#ifndef CPATTN_H
+#define CPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CPATTN_ABI_VERSION 1
+
+enum {
+  CPATTN_OK = 0,
+  CPATTN_EINVAL = -1,      /* invalid argument (null pointer, bad shape or stride, bad map) */
+  CPATTN_EUNSUPPORTED = -2, /* valid but not implemented (e.g. D not 64 or 128) */
+  CPATTN_EHIP = -3          /* a HIP launch failed */
+};
+
+enum { CPATTN_F32 = 0, CPATTN_BF16 = 1 };
+
+typedef struct {
+  int64_t len, split, d0, d1;
+} cpattn_posmap;
+
+typedef struct {
+  void* data;
+  int64_t sb, sh, st;
+} cpattn_tensor;
+
+/* ABI version (CPATTN_ABI_VERSION). */
+int cpattn_version(void);
+
+/* Message for the last non-zero status returned on this thread ("" if none). */
+const char* cpattn_last_error(void);
+
+/*
+ * HeadTail shard map (host only, integer, exact).
+ * The global sequence of T tokens is cut into 2*ring chunks of c = T/(2*ring)
+ * tokens; rank r holds chunk r followed by chunk 2*ring-1-r (BluScriptCP log,
+ * 2026-05-16 and 2026-06-29: Megatron's chunk pair [r, 2cp-1-r]; the worked
+ * example with two ranks and eight tokens gives rank 0 positions 0, 1, 6, 7).
+ *   map        out: len = 2c, split = c, d0 = r*c, d1 = (2*ring-2-r)*c
+ *   positions  out, nullable: host int32 array of 2c global positions
+ * Errors: EINVAL if T <= 0, ring <= 0, T % (2*ring) != 0, rank outside
+ * [0, ring), T >= 2^31, or map is NULL.
+ */
+int cpattn_headtail_shard(int64_t T, int32_t ring, int32_t rank,
+                          cpattn_posmap* map, int32_t* positions);
+
+/*
+ * Rotary table: table[p][i] = (cos a, sin a), a = p * theta^(-2i/D), for
+ * p in [0, rows), i in [0, D/2); fp32 values of angles computed in fp64 on
+ * the device. table is a device array of rows*D floats (interleaved pairs).
+ * Reading of the rotary form used with it: dimension i pairs with i + D/2
+ * (half-split), as in the Llama-style fused rotary of the BluScriptCP log
+ * (2026-07-02), at global positions (2026-06-29).
+ * Errors: EINVAL if theta <= 0, rows <= 0, D odd or <= 0, table NULL.
+ */
+int cpattn_rope_table(double theta, int64_t rows, int64_t D, float* table, void* stream);
+
+/*
+ * Block forward: attention of local query rows [row_begin, row_end) of q
+ * ([B,H,Tq,D]) against one KV block k, v ([B,H,Tk,D]) at global positions
+ * qmap/kmap. Writes fp32 o [B,H,Tq,D] and lse [B,H,Tq] for those rows only.
+ *   dtype       CPATTN_BF16 (bf16 inputs, MFMA with fp32 accumulation) or
+ *               CPATTN_F32 (fp32 inputs and arithmetic); q, k, v share it
+ *   rope_table  nullable: if set (bf16 only), q and k rows are rotated by the
+ *               table row of their global position before the products;
+ *               rope_rows = rows in the table, every position must be below it
+ * Errors: EINVAL for null tensors, D stride assumptions broken, a map whose
+ * len differs from Tq/Tk or with d1 < d0, an empty or out-of-range row range,
+ * positions outside the rotary table; EUNSUPPORTED for D not in {64, 128} or
+ * a rotary table with fp32 inputs.
+ */
+int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                     int32_t dtype, int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
+                     const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                     float scale, const float* rope_table, int64_t rope_rows,
+                     int64_t row_begin, int64_t row_end,
+                     const cpattn_tensor* o, const cpattn_tensor* lse, void* stream);
+
+/*
+ * SDPAMerger: for rows [row_begin, row_end) of every (b, h), fold the block
+ * result (o_blk, lse_blk) into the running result (o_acc, lse_acc), in place:
+ *   L = log(exp(L_acc) + exp(L_blk)),
+ *   O = exp(L_acc - L) O_acc + exp(L_blk - L) O_blk.
+ * A side with LSE = -inf is the identity; both -inf give (0, -inf).
+ * All four tensors are fp32: o_* [B,H,T,D], lse_* [B,H,T].
+ * Errors: EINVAL for null tensors or a bad row range; EUNSUPPORTED if D % 4.
+ */
+int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc,
+                     const cpattn_tensor* o_blk, const cpattn_tensor* lse_blk,
+                     int64_t B, int64_t H, int64_t T, int64_t D,
+                     int64_t row_begin, int64_t row_end, void* stream);
+
+/* Workspace bytes cpattn_ring_fwd needs: an fp32 block output and LSE. */
+size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D);
+
+/*
+ * Ring forward of rank `rank` out of `ring`, all KV blocks resident in HBM.
+ * k_blocks[i], v_blocks[i], kmaps[i] describe the block owned by rank i
+ * (each [B,H,Tk,D]). At step s the rank holds the block of owner
+ * (rank - s) mod ring (blocks travel to the next rank each step). Step 0
+ * writes (o_acc, lse_acc) directly; every later step runs the block forward
+ * on the rows that see at least one key of that block, into the workspace,
+ * then merges those rows. Steps whose block is invisible to every row are
+ * skipped. At most two launches per step, no synchronisation.
+ * workspace: device memory of cpattn_ring_fwd_workspace_bytes(B,H,Tq,D)
+ * bytes, 256-byte aligned. Other arguments as in cpattn_block_fwd.
+ * Errors: as cpattn_block_fwd, plus EINVAL for ring < 1, rank out of range,
+ * a short workspace.
+ */
+int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks,
+                    const cpattn_tensor* v_blocks, const cpattn_posmap* kmaps,
+                    int32_t ring, int32_t rank, const cpattn_posmap* qmap, int32_t dtype,
+                    int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t causal,
+                    float scale, const float* rope_table, int64_t rope_rows,
+                    const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward preprocess: delta[b,h,p] = sum_d dout[b,h,p,d] * o[b,h,p,d]
+ * (the row term of the softmax backward; BluScriptCP log, 2026-03-24, the
+ * Di correction), with o the final merged fp32 output.
+ * dout has `dtype` (bf16 or fp32); o, delta fp32.
+ */
+int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* o,
+                          const cpattn_tensor* delta, int64_t B, int64_t H, int64_t Tq, int64_t D,
+                          void* stream);
+
+/*
+ * Block backward of one ring step: with the FINAL merged lse and delta of the
+ * local query rows, recompute P = exp(scale * q k^T - lse) over the visible
+ * pairs of this block and ADD into fp32 accumulators:
+ *   dv_acc += P^T dout
+ *   dS      = P * (dout v^T - delta)
+ *   dq_acc += scale * dS k
+ *   dk_acc += scale * dS^T q
+ * dq_acc is [B,H,Tq,D] (the local rows), dk_acc and dv_acc are [B,H,Tk,D]
+ * (the block's rows). The caller zeroes them once before the first step and
+ * never between steps. bf16 inputs only; rotary is not supported here.
+ * Two kernels (key-tile-major for dk/dv, query-tile-major for dq), no atomics:
+ * results are bitwise reproducible.
+ * Errors: as cpattn_block_fwd; EUNSUPPORTED for fp32 inputs.
+ */
+int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                     const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                     const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
+                     const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
+                     int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
+                     const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                     float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPATTN_H */

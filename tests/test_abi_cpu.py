@@ -1,0 +1,140 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, the host-only shard map is bit-exact against the oracle's independent
+map, and invalid arguments are rejected before any launch.
+
+No call here reaches a kernel: every argument set is invalid, so the library
+returns an error code during validation.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import context_causal_attention_cpattn_amd as cp
+from oracle import shard
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(cp.lib_path), reason="libcpattn.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cp.load()
+    syms = declared_symbols()
+    assert len(syms) >= 10
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert set(syms) == set(cp.EXPORTS)
+
+
+def test_version():
+    assert cp.cpattn_version() == 1
+
+
+@pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
+def test_headtail_shard_bit_exact(T, ring):
+    for r in range(ring):
+        (L, split, d0, d1), pos = cp.cpattn_headtail_shard(T, ring, r)
+        assert pos == shard.headtail_positions(T, ring, r)
+        assert (L, split, d0, d1) == shard.headtail_deltas(T, ring, r)
+
+
+def test_headtail_shard_worked_example():
+    _, pos = cp.cpattn_headtail_shard(8, 2, 0)
+    assert pos == [0, 1, 6, 7]
+
+
+@pytest.mark.parametrize("T,ring,rank", [(10, 2, 0), (8, 2, 2), (8, 2, -1), (0, 1, 0), (8, 0, 0), (2 ** 31, 1, 0)])
+def test_headtail_shard_rejects(T, ring, rank):
+    lib = cp.load()
+    m = cp.cpattn_posmap()
+    assert lib.cpattn_headtail_shard(T, ring, rank, ctypes.byref(m), None) == -1
+    assert cp.cpattn_last_error() != ""
+
+
+def _t(addr=0x10000, sb=0, sh=0, st=64):
+    return cp.cpattn_tensor(addr, sb, sh, st)
+
+
+def _fwd(lib, **kw):
+    args = dict(q=_t(), k=_t(), v=_t(), dtype=1, B=1, H=1, Tq=64, Tk=64, D=64, qmap=cp.cpattn_posmap(64, 64, 0, 0),
+                kmap=cp.cpattn_posmap(64, 64, 0, 0), causal=1, scale=0.0, rope=None, rope_rows=0, rb=0, re=64,
+                o=_t(), lse=_t(st=1))
+    args.update(kw)
+    a = args
+    return lib.cpattn_block_fwd(ctypes.byref(a["q"]) if a["q"] is not None else None, ctypes.byref(a["k"]),
+                                ctypes.byref(a["v"]), a["dtype"], a["B"], a["H"], a["Tq"], a["Tk"], a["D"],
+                                ctypes.byref(a["qmap"]), ctypes.byref(a["kmap"]), a["causal"], a["scale"], a["rope"],
+                                a["rope_rows"], a["rb"], a["re"], ctypes.byref(a["o"]), ctypes.byref(a["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(D=96), -2),
+    (dict(D=0), -1),
+    (dict(dtype=7), -1),
+    (dict(q=_t(addr=0x10002)), -1),               # misaligned
+    (dict(k=_t(st=60)), -1),                      # bf16 row stride not a multiple of 8
+    (dict(qmap=cp.cpattn_posmap(63, 32, 0, 0)), -1),  # len != Tq
+    (dict(kmap=cp.cpattn_posmap(64, 32, 10, 0)), -1),  # d1 < d0
+    (dict(kmap=cp.cpattn_posmap(64, 70, 0, 0)), -1),   # split > len
+    (dict(rb=10, re=10), -1),                     # empty row range
+    (dict(rb=0, re=65), -1),                      # beyond Tq
+    (dict(scale=-1.0), -1),
+    (dict(rope=ctypes.c_void_p(0x20000), rope_rows=32), -1),  # positions beyond the table
+    (dict(dtype=0, rope=ctypes.c_void_p(0x20000), rope_rows=1000), -2),  # rotary with fp32
+])
+def test_block_fwd_rejects_before_launch(kw, code):
+    lib = cp.load()
+    assert _fwd(lib, **kw) == code
+    assert cp.cpattn_last_error() != ""
+
+
+def test_ring_fwd_rejects():
+    lib = cp.load()
+    n = 2
+    ks = (cp.cpattn_tensor * n)(_t(), _t())
+    ms = (cp.cpattn_posmap * n)(cp.cpattn_posmap(64, 32, 0, 64), cp.cpattn_posmap(64, 32, 32, 32))
+    qm = cp.cpattn_posmap(64, 32, 0, 64)
+    o, lse = _t(), _t(st=1)
+    args = lambda ring, rank, ws, wsb: (ctypes.byref(_t()), ks, ks, ms, ring, rank, ctypes.byref(qm), 1, 1, 1, 64, 64,
+                                        64, 1, 0.0, None, 0, ctypes.byref(o), ctypes.byref(lse), ws, wsb, None)
+    assert lib.cpattn_ring_fwd(*args(0, 0, None, 0)) == -1
+    assert lib.cpattn_ring_fwd(*args(2, 2, None, 0)) == -1
+    assert lib.cpattn_ring_fwd(*args(2, 0, None, 0)) == -1  # no workspace
+    assert lib.cpattn_ring_fwd(*args(2, 0, ctypes.c_void_p(0x100010), 1 << 20)) == -1  # misaligned workspace
+    assert "workspace" in cp.cpattn_last_error()
+
+
+def test_ring_workspace_size():
+    assert cp.cpattn_ring_fwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 128 * 4 + 32 * 8192 * 4
+    assert cp.cpattn_ring_fwd_workspace_bytes(0, 1, 1, 1) == 0
+
+
+def test_merge_and_bwd_reject():
+    lib = cp.load()
+    t, l3 = _t(), _t(st=1)
+    assert lib.cpattn_lse_merge(ctypes.byref(t), ctypes.byref(l3), ctypes.byref(t), ctypes.byref(l3), 1, 1, 64, 64,
+                                5, 5, None) == -1
+    assert lib.cpattn_lse_merge(ctypes.byref(t), ctypes.byref(l3), ctypes.byref(t), ctypes.byref(l3), 1, 1, 64, 48,
+                                0, 64, None) == -2
+    m = cp.cpattn_posmap(64, 64, 0, 0)
+    bt = ctypes.byref(t)
+    assert lib.cpattn_block_bwd(bt, bt, bt, bt, 0, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1, 1, 64, 64, 64,
+                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -2  # fp32 backward
+    assert lib.cpattn_bwd_preprocess(bt, 3, bt, ctypes.byref(l3), 1, 1, 64, 64, None) == -1
+
+
+def test_rope_table_rejects():
+    lib = cp.load()
+    assert lib.cpattn_rope_table(0.0, 10, 128, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.cpattn_rope_table(10000.0, 10, 127, ctypes.c_void_p(0x1000), None) == -1
+    assert lib.cpattn_rope_table(10000.0, 10, 128, None, None) == -1

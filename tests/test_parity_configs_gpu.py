@@ -1,0 +1,157 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times (the ring driver, then the backward preprocess and one block
+backward per ring step), against the fp64 oracle.
+
+The kernels always run on every head; for the large workloads the oracle
+recomputes a sample of heads in full (every row and column of those heads).
+"""
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_cpattn_amd as cp
+from oracle import attention as oa
+from oracle import rope as orope
+from workloads import BY_NAME, draw
+
+from _util import TOL_BF16, TOL_F32, f64, gather, log, max_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+class Share:
+    """One rank's share of the ring on the GPU (all KV blocks resident)."""
+
+    def __init__(self, w, t, rank, rope=False):
+        self.w, self.rank = w, rank
+        N = w.ring
+        self.maps, self.pos = zip(*[cp.cpattn_headtail_shard(w.T, N, r) for r in range(N)])
+        self.kb = [gather(t["k"], p) for p in self.pos]
+        self.vb = [gather(t["v"], p) for p in self.pos]
+        self.q = gather(t["q"], self.pos[rank])
+        self.do = gather(t["do"], self.pos[rank]) if "do" in t else None
+        Tl = w.local_len
+        self.tab = None
+        if rope:
+            self.tab = torch.empty(w.T, w.D, device=DEV)
+            cp.cpattn_rope_table(w.rope_theta, w.T, w.D, self.tab)
+        self.ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(w.B, w.H, Tl, w.D), dtype=torch.uint8, device=DEV)
+        self.o = torch.empty(w.B, w.H, Tl, w.D, device=DEV)
+        self.lse = torch.empty(w.B, w.H, Tl, device=DEV)
+
+    def forward(self):
+        cp.cpattn_ring_fwd(self.q, self.kb, self.vb, self.maps, self.rank, self.maps[self.rank], self.o, self.lse,
+                           self.ws, rope_table=self.tab)
+
+    def backward(self, dk, dv):
+        w, N, r = self.w, self.w.ring, self.rank
+        self.delta = torch.empty(w.B, w.H, w.local_len, device=DEV)
+        cp.cpattn_bwd_preprocess(self.do, self.o, self.delta)
+        self.dq = torch.zeros_like(self.o)
+        for s in range(N):
+            src = (r - s) % N
+            cp.cpattn_block_bwd(self.q, self.kb[src], self.vb[src], self.do, self.lse, self.delta, self.dq, dk[src],
+                                dv[src], self.maps[r], self.maps[src])
+
+
+def check_fwd(share, t64, heads, tol, rope_theta=0.0):
+    rows = list(share.pos[share.rank])
+    q, k, v = t64["q"], t64["k"], t64["v"]
+    if rope_theta:
+        allpos = np.arange(q.shape[2])
+        q, k = orope.rope_apply(q, allpos, rope_theta), orope.rope_apply(k, allpos, rope_theta)
+    O, L = oa.causal_attention_fwd(q, k, v, rows=rows)
+    eo = max_err(f64(share.o[:, heads]), O)
+    el = max_err(f64(share.lse[:, heads]), L)
+    log(f"  rank {share.rank}: max err O {eo:.3g} LSE {el:.3g} (heads {heads})")
+    assert eo <= tol and el <= tol
+    return O, L
+
+
+def test_tiny_fp32_both_ranks():
+    w = BY_NAME["tiny"]
+    log(f"workload {w.name}")
+    t = draw(w)
+    t64 = {n: f64(x) for n, x in t.items()}
+    for r in range(w.ring):
+        s = Share(w, t, r)
+        s.forward()
+        torch.cuda.synchronize()
+        check_fwd(s, t64, slice(None), TOL_F32)
+
+
+def test_gpt2s_rank0_forward_and_backward():
+    w = BY_NAME["gpt2s"]
+    log(f"workload {w.name}")
+    g = torch.Generator().manual_seed(w.seed + 1000)
+    t = draw(w)
+    t["do"] = torch.randn(w.B, w.H, w.T, w.D, generator=g).to(torch.bfloat16)
+    t64 = {n: f64(x) for n, x in t.items()}
+    s = Share(w, t, 0)
+    dk = [torch.zeros(w.B, w.H, w.local_len, w.D, device=DEV) for _ in range(w.ring)]
+    dv = [torch.zeros_like(x) for x in dk]
+    s.forward()
+    s.backward(dk, dv)
+    torch.cuda.synchronize()
+    O, L = check_fwd(s, t64, slice(None), TOL_BF16)
+    rows = list(s.pos[0])
+    gq, gk, gv = oa.block_attention_bwd(t64["q"][:, :, rows], t64["k"], t64["v"], t64["do"][:, :, rows], O, L, rows,
+                                        np.arange(w.T))
+    e = [max_err(f64(s.dq), gq)]
+    for src in range(w.ring):
+        p = list(s.pos[src])
+        e += [max_err(f64(dk[src]), gk[:, :, p]), max_err(f64(dv[src]), gv[:, :, p])]
+    log(f"  rank-0 backward share: max err dq {e[0]:.3g} dk/dv {max(e[1:]):.3g}")
+    assert max(e) <= TOL_BF16
+
+
+def test_win16k_rank0_forward():
+    w = BY_NAME["win16k"]
+    log(f"workload {w.name}")
+    t = draw(w)
+    s = Share(w, t, 0)
+    s.forward()
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
+    check_fwd(s, t64, heads, TOL_BF16)
+
+
+def test_win32k_rope_rank0_forward():
+    w = BY_NAME["win32k"]
+    log(f"workload {w.name}")
+    t = draw(w)
+    s = Share(w, t, 0, rope=True)
+    s.forward()
+    torch.cuda.synchronize()
+    heads = [9]
+    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
+    check_fwd(s, t64, heads, TOL_BF16, rope_theta=w.rope_theta)
+
+
+def test_bwd16k_all_ranks():
+    w = BY_NAME["bwd16k"]
+    log(f"workload {w.name}")
+    t = draw(w)
+    dk = [torch.zeros(w.B, w.H, w.local_len, w.D, device=DEV) for _ in range(w.ring)]
+    dv = [torch.zeros_like(x) for x in dk]
+    shares = []
+    for r in range(w.ring):
+        s = Share(w, t, r)
+        s.forward()
+        s.backward(dk, dv)
+        shares.append(s)
+    torch.cuda.synchronize()
+    heads = [3]
+    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
+    dQ, dK, dV, O, L = oa.causal_attention_bwd(t64["q"], t64["k"], t64["v"], t64["do"])
+    for s in shares:
+        rows = list(s.pos[s.rank])
+        eo = max_err(f64(s.o[:, heads]), O[:, :, rows])
+        el = max_err(f64(s.lse[:, heads]), L[:, :, rows])
+        eq = max_err(f64(s.dq[:, heads]), dQ[:, :, rows])
+        ek = max_err(f64(dk[s.rank][:, heads]), dK[:, :, rows])
+        ev = max_err(f64(dv[s.rank][:, heads]), dV[:, :, rows])
+        log(f"  rank {s.rank}: O {eo:.3g} LSE {el:.3g} dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
+        assert max(eo, el, eq, ek, ev) <= TOL_BF16

@@ -1,0 +1,280 @@
+"""GPU parity of each entry point against the fp64 oracle at sizes the oracle
+finishes in seconds, spanning several tiles and a ragged tail, plus edge cases.
+
+Every kernel result is compared element by element with the oracle on the
+same seeded inputs (bf16 inputs: the oracle receives the rounded values).
+"""
+import numpy as np
+import pytest
+import torch
+
+import context_causal_attention_cpattn_amd as cp
+from oracle import attention as oa
+from oracle import merge as om
+from oracle import rope as orope
+from oracle import shard as osh
+from workloads import draw_shape
+
+from _util import TOL_BF16, TOL_F32, f64, gather, log, max_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def positions(m):
+    L, split, d0, d1 = m
+    return np.array([i + (d0 if i < split else d1) for i in range(L)])
+
+
+def tol(dtype):
+    return TOL_F32 if dtype == torch.float32 else TOL_BF16
+
+
+# ----------------------------------------------------------------------------- merge
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rb,re", [(0, 333), (97, 250)])
+def test_lse_merge(D, rb, re):
+    log(f"merge D={D} rows [{rb},{re})")
+    B, H, T = 2, 3, 333
+    g = torch.Generator().manual_seed(D + rb)
+    oa_, ob_ = torch.randn(B, H, T, D, generator=g), torch.randn(B, H, T, D, generator=g)
+    la_, lb_ = torch.randn(B, H, T, generator=g) * 3, torch.randn(B, H, T, generator=g) * 3
+    la_[:, :, ::7] = -float("inf")
+    lb_[:, :, ::5] = -float("inf")
+    # strided accumulators: every other row of a larger buffer
+    big_o = torch.zeros(B, H, 2 * T, D, device=DEV)
+    big_l = torch.zeros(B, H, 2 * T, device=DEV)
+    o_acc, l_acc = big_o[:, :, ::2], big_l[:, :, ::2]
+    o_acc.copy_(oa_)
+    l_acc.copy_(la_)
+    cp.cpattn_lse_merge(o_acc, l_acc, ob_.to(DEV), lb_.to(DEV), rb, re)
+    torch.cuda.synchronize()
+    O, L = om.lse_merge(f64(oa_)[:, :, rb:re], f64(la_)[:, :, rb:re], f64(ob_)[:, :, rb:re], f64(lb_)[:, :, rb:re])
+    got_o, got_l = f64(o_acc), f64(l_acc)
+    assert max_err(got_o[:, :, rb:re], O) <= 1e-5
+    assert max_err(got_l[:, :, rb:re], L) <= 1e-5
+    # rows outside the range are untouched
+    assert np.array_equal(got_o[:, :, :rb], f64(oa_)[:, :, :rb]) and np.array_equal(got_o[:, :, re:], f64(oa_)[:, :, re:])
+    assert np.array_equal(got_l[:, :, :rb], f64(la_)[:, :, :rb])
+    assert (f64(big_o)[:, :, 1::2] == 0).all()
+
+
+# ----------------------------------------------------------------------------- block forward
+
+FWD_CASES = [
+    # B, H, Tq, Tk, D, qmap, kmap, causal, rows
+    (1, 2, 300, 200, 128, (300, 150, 1000, 1300), (200, 100, 900, 1200), True, None),   # seams, ragged
+    (2, 1, 256, 320, 64, (256, 128, 512, 1024), (320, 160, 400, 800), True, None),
+    (1, 3, 190, 130, 128, (190, 190, 0, 0), (130, 130, 0, 0), False, None),           # non-causal, ragged
+    (1, 2, 257, 257, 64, (257, 257, 0, 0), (257, 257, 0, 0), True, (37, 201)),        # row range
+    (1, 1, 128, 128, 128, (128, 64, 0, 192), (128, 64, 64, 64), True, None),          # LEFT-half shape
+    (1, 1, 128, 128, 128, (128, 64, 0, 192), (128, 64, 128, 128), True, None),        # tail rows only
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", range(len(FWD_CASES)))
+def test_block_fwd(case, dtype):
+    B, H, Tq, Tk, D, qm, km, causal, rows = FWD_CASES[case]
+    log(f"block_fwd case {case} dtype {dtype}")
+    q, = draw_shape(B, H, Tq, D, dtype, seed=10 + case, n=1)
+    k, v = draw_shape(B, H, Tk, D, dtype, seed=20 + case, n=2)
+    rb, re = rows if rows else (0, Tq)
+    o = torch.full((B, H, Tq, D), 7.0, device=DEV)
+    lse = torch.full((B, H, Tq), 7.0, device=DEV)
+    cp.cpattn_block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), qm, km, o, lse, causal=causal, row_begin=rb, row_end=re)
+    torch.cuda.synchronize()
+    O, L = oa.block_attention_fwd(f64(q)[:, :, rb:re], f64(k), f64(v), positions(qm)[rb:re], positions(km), causal)
+    eo, el = max_err(f64(o)[:, :, rb:re], O), max_err(f64(lse)[:, :, rb:re], L)
+    log(f"  max err O {eo:.3g} LSE {el:.3g}")
+    assert eo <= tol(dtype) and el <= tol(dtype)
+    assert (f64(o)[:, :, :rb] == 7).all() and (f64(o)[:, :, re:] == 7).all()
+    assert (f64(lse)[:, :, :rb] == 7).all() and (f64(lse)[:, :, re:] == 7).all()
+
+
+def test_block_fwd_strided_inputs():
+    # q/k/v as head-major views of a [B, T, H, D] buffer (non-contiguous B/H/T strides)
+    B, H, T, D = 2, 4, 200, 128
+    log("block_fwd strided")
+    base = draw_shape(B, T, H, D, torch.bfloat16, seed=5, n=3)
+    q, k, v = (x.to(DEV).transpose(1, 2) for x in base)
+    m = (T, 100, 0, 300)
+    o = torch.empty(B, T, H, D, device=DEV).transpose(1, 2)
+    lse = torch.empty(B, T, H, device=DEV).transpose(1, 2)
+    cp.cpattn_block_fwd(q, k, v, m, m, o, lse)
+    torch.cuda.synchronize()
+    O, L = oa.block_attention_fwd(f64(q), f64(k), f64(v), positions(m), positions(m))
+    assert max_err(f64(o), O) <= TOL_BF16 and max_err(f64(lse), L) <= TOL_BF16
+
+
+def test_block_fwd_dead_rows_and_single_token():
+    log("block_fwd dead rows / single token")
+    q, k, v = draw_shape(1, 1, 64, 64, torch.bfloat16, seed=3, n=3)
+    o = torch.empty(1, 1, 64, 64, device=DEV)
+    lse = torch.empty(1, 1, 64, device=DEV)
+    # every key is in the future of every query
+    cp.cpattn_block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), (64, 64, 0, 0), (64, 64, 1000, 1000), o, lse)
+    torch.cuda.synchronize()
+    assert (f64(o) == 0).all() and np.isneginf(f64(lse)).all()
+    for dtype in (torch.bfloat16, torch.float32):
+        q1, k1, v1 = draw_shape(1, 2, 1, 128, dtype, seed=4, n=3)
+        o1 = torch.empty(1, 2, 1, 128, device=DEV)
+        l1 = torch.empty(1, 2, 1, device=DEV)
+        cp.cpattn_block_fwd(q1.to(DEV), k1.to(DEV), v1.to(DEV), (1, 1, 5, 5), (1, 1, 5, 5), o1, l1)
+        torch.cuda.synchronize()
+        # one visible key: O = v, LSE = sigma q.k
+        assert max_err(f64(o1), f64(v1)) <= tol(dtype)
+        ref = (f64(q1) * f64(k1)).sum(-1) / np.sqrt(128)
+        assert max_err(f64(l1), ref) <= tol(dtype)
+
+
+# ----------------------------------------------------------------------------- rotary
+
+def test_rope_table():
+    log("rope table")
+    rows, D = 40000, 128
+    t = torch.empty(rows * D, device=DEV)
+    cp.cpattn_rope_table(10000.0, rows, D, t)
+    torch.cuda.synchronize()
+    a = orope.rope_angles(np.arange(rows), D, 10000.0)
+    got = f64(t).reshape(rows, D // 2, 2)
+    assert np.abs(got[..., 0] - np.cos(a)).max() <= 1e-6
+    assert np.abs(got[..., 1] - np.sin(a)).max() <= 1e-6
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_fwd_rope(D):
+    log(f"block_fwd rope D={D}")
+    B, H, Tq, Tk = 1, 2, 200, 300
+    q, = draw_shape(B, H, Tq, D, torch.bfloat16, seed=30, n=1)
+    k, v = draw_shape(B, H, Tk, D, torch.bfloat16, seed=31, n=2)
+    qm, km = (200, 100, 5000, 20000), (300, 150, 4000, 19000)
+    rows = 20500
+    tab = torch.empty(rows, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, rows, D, tab)
+    o = torch.empty(B, H, Tq, D, device=DEV)
+    lse = torch.empty(B, H, Tq, device=DEV)
+    cp.cpattn_block_fwd(q.to(DEV), k.to(DEV), v.to(DEV), qm, km, o, lse, rope_table=tab)
+    torch.cuda.synchronize()
+    qp, kp = positions(qm), positions(km)
+    qr, kr = orope.rope_apply(f64(q), qp, 10000.0), orope.rope_apply(f64(k), kp, 10000.0)
+    O, L = oa.block_attention_fwd(qr, kr, f64(v), qp, kp)
+    eo, el = max_err(f64(o), O), max_err(f64(lse), L)
+    log(f"  max err O {eo:.3g} LSE {el:.3g}")
+    assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
+# ----------------------------------------------------------------------------- ring forward
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,N,D", [(400, 2, 128), (600, 3, 64), (256, 2, 64)])
+def test_ring_fwd_all_ranks(T, N, D, dtype):
+    log(f"ring_fwd T={T} N={N} D={D} {dtype}")
+    B, H = 1, 2
+    q, k, v = draw_shape(B, H, T, D, dtype, seed=T + N, n=3)
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, r) for r in range(N)])
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    Tl = T // N
+    ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(B, H, Tl, D), dtype=torch.uint8, device=DEV)
+    O, L = oa.causal_attention_fwd(f64(q), f64(k), f64(v))
+    for r in range(N):
+        o = torch.empty(B, H, Tl, D, device=DEV)
+        lse = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_ring_fwd(gather(q, pos[r]), kb, vb, maps, r, maps[r], o, lse, ws)
+        torch.cuda.synchronize()
+        eo, el = max_err(f64(o), O[:, :, list(pos[r])]), max_err(f64(lse), L[:, :, list(pos[r])])
+        log(f"  rank {r}: max err O {eo:.3g} LSE {el:.3g}")
+        assert eo <= tol(dtype) and el <= tol(dtype)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def run_ring_bwd(q, k, v, do, N, causal=True):
+    """All ranks' shares through the library; returns global-order dq, dk, dv (fp64 numpy)."""
+    B, H, T, D = q.shape
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, r) for r in range(N)])
+    Tl = T // N
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(B, H, Tl, D), dtype=torch.uint8, device=DEV)
+    dk = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(N)]
+    dv = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(N)]
+    gq = np.zeros((B, H, T, D))
+    gk = np.zeros((B, H, T, D))
+    gv = np.zeros((B, H, T, D))
+    for r in range(N):
+        qr, dor = gather(q, pos[r]), gather(do, pos[r])
+        o = torch.empty(B, H, Tl, D, device=DEV)
+        lse = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_ring_fwd(qr, kb, vb, maps, r, maps[r], o, lse, ws, causal=causal)
+        delta = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_bwd_preprocess(dor, o, delta)
+        dq = torch.zeros(B, H, Tl, D, device=DEV)
+        for s in range(N):
+            src = (r - s) % N
+            cp.cpattn_block_bwd(qr, kb[src], vb[src], dor, lse, delta, dq, dk[src], dv[src], maps[r], maps[src],
+                                causal=causal)
+        torch.cuda.synchronize()
+        gq[:, :, list(pos[r])] = f64(dq)
+    for r in range(N):
+        gk[:, :, list(pos[r])] = f64(dk[r])
+        gv[:, :, list(pos[r])] = f64(dv[r])
+    return gq, gk, gv
+
+
+@pytest.mark.parametrize("T,N,D", [(400, 2, 128), (600, 3, 64), (512, 2, 128)])
+def test_ring_bwd_all_ranks(T, N, D):
+    log(f"ring_bwd T={T} N={N} D={D}")
+    q, k, v, do = draw_shape(1, 2, T, D, torch.bfloat16, seed=T * 3 + N, n=4)
+    gq, gk, gv = run_ring_bwd(q, k, v, do, N)
+    dQ, dK, dV, _, _ = oa.causal_attention_bwd(f64(q), f64(k), f64(v), f64(do))
+    e = (max_err(gq, dQ), max_err(gk, dK), max_err(gv, dV))
+    log(f"  max err dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    assert max(e) <= TOL_BF16
+
+
+def test_block_bwd_noncausal_ragged():
+    log("block_bwd non-causal ragged")
+    B, H, Tq, Tk, D = 1, 2, 150, 230, 128
+    q, do = draw_shape(B, H, Tq, D, torch.bfloat16, seed=40, n=2)
+    k, v = draw_shape(B, H, Tk, D, torch.bfloat16, seed=41, n=2)
+    qm, km = (Tq, Tq, 0, 0), (Tk, Tk, 0, 0)
+    qp, kp = positions(qm), positions(km)
+    O, L = oa.block_attention_fwd(f64(q), f64(k), f64(v), qp, kp, causal=False)
+    o = torch.tensor(O, dtype=torch.float32, device=DEV)
+    lse = torch.tensor(L, dtype=torch.float32, device=DEV)
+    delta = torch.empty(B, H, Tq, device=DEV)
+    cp.cpattn_bwd_preprocess(do.to(DEV), o, delta)
+    dq = torch.zeros(B, H, Tq, D, device=DEV)
+    dk = torch.zeros(B, H, Tk, D, device=DEV)
+    dv = torch.zeros(B, H, Tk, D, device=DEV)
+    cp.cpattn_block_bwd(q.to(DEV), k.to(DEV), v.to(DEV), do.to(DEV), lse, delta, dq, dk, dv, qm, km, causal=False)
+    torch.cuda.synchronize()
+    assert max_err(f64(delta), oa.delta(f64(do), O)) <= 1e-4
+    gq, gk, gv = oa.block_attention_bwd(f64(q), f64(k), f64(v), f64(do), O, L, qp, kp, causal=False)
+    e = (max_err(f64(dq), gq), max_err(f64(dk), gk), max_err(f64(dv), gv))
+    log(f"  max err dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    assert max(e) <= TOL_BF16
+
+
+def test_bwd_preprocess_fp32_and_bf16():
+    log("bwd_preprocess")
+    for dtype in (torch.float32, torch.bfloat16):
+        for D in (64, 128):
+            do, = draw_shape(2, 3, 77, D, dtype, seed=D, n=1)
+            o, = draw_shape(2, 3, 77, D, torch.float32, seed=D + 1, n=1)
+            delta = torch.empty(2, 3, 77, device=DEV)
+            cp.cpattn_bwd_preprocess(do.to(DEV), o.to(DEV), delta)
+            torch.cuda.synchronize()
+            assert max_err(f64(delta), oa.delta(f64(do), f64(o))) <= 1e-4
+
+
+def test_determinism_bitwise():
+    log("determinism")
+    q, k, v, do = draw_shape(1, 2, 512, 128, torch.bfloat16, seed=99, n=4)
+    a = run_ring_bwd(q, k, v, do, 2)
+    b = run_ring_bwd(q, k, v, do, 2)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
