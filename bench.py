@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Benchmark of one rank's share of causal ring attention under HeadTail sharding.
+
+A step is one pass of the whole hot path over one batch of synthetic input,
+for rank 0 of the GPT-2-small-shaped workload (B=4, H=12, D=64, T=4096, ring
+degree 4; bf16 inputs, fp32 accumulation), with every KV block resident in HBM:
+
+  * for each ring step s (block owner src = -s mod 4): classify the step
+    (cpattn_step_rows), block forward of the visible rows (step 0 straight into
+    the accumulator), LSE merge of those rows (steps >= 1);
+  * backward preprocess delta = rowsum(dO * O);
+  * for each ring step: dK/dV kernel then dQ kernel, accumulating in fp32
+    (accumulators cleared once at the start of the step).
+
+Throughput is causal-effective: only visible (query, key) pairs count, at
+4*D flops per pair for the forward and 10*D for the backward. Every launch of
+the timed steps is bracketed by HIP events on the stream the library runs on,
+which gives each kernel's average duration for the roofline object. The fp64
+CPU oracle is timed on a bounded sample of the same workload for the
+cpu_baseline object.
+
+Prints ONE JSON line. Only one GPU is supported.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic per launch of the dominant kernel (from rocprofv3 --pmc)")
+    return ap.parse_args()
+
+
+class Share:
+    """Rank 0's share of a workload on the GPU: shards, blocks, accumulators."""
+
+    def __init__(self, w, seed_do: int):
+        import torch
+
+        import context_causal_attention_cpattn_amd as cp
+        from workloads import draw
+        self.cp, self.w = cp, w
+        dev = torch.device("cuda:0")
+        t = draw(w)
+        if "do" not in t:
+            g = torch.Generator().manual_seed(seed_do)
+            t["do"] = torch.randn(w.B, w.H, w.T, w.D, generator=g).to(w.torch_dtype)
+        self.host = t
+        N = w.ring
+        self.maps, self.pos = zip(*[cp.cpattn_headtail_shard(w.T, N, r) for r in range(N)])
+        idx = lambda r: torch.as_tensor(self.pos[r], dtype=torch.long)
+        loc = lambda x, r: x.index_select(2, idx(r)).contiguous().to(dev)
+        self.kb = [loc(t["k"], r) for r in range(N)]
+        self.vb = [loc(t["v"], r) for r in range(N)]
+        self.q = loc(t["q"], 0)
+        self.do = loc(t["do"], 0)
+        Tl = w.local_len
+        self.tab = None
+        if w.rope_theta:
+            self.tab = torch.empty(w.T, w.D, device=dev)
+            cp.cpattn_rope_table(w.rope_theta, w.T, w.D, self.tab)
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.o = torch.empty(w.B, w.H, Tl, w.D, **f32)
+        self.lse = torch.empty(w.B, w.H, Tl, **f32)
+        self.o_blk = torch.empty(w.B, w.H, Tl, w.D, **f32)
+        self.l_blk = torch.empty(w.B, w.H, Tl, **f32)
+        self.delta = torch.empty(w.B, w.H, Tl, **f32)
+        self.dq = torch.zeros(w.B, w.H, Tl, w.D, **f32)
+        self.dk = [torch.zeros(w.B, w.H, Tl, w.D, **f32) for _ in range(N)]
+        self.dv = [torch.zeros(w.B, w.H, Tl, w.D, **f32) for _ in range(N)]
+        # per ring step: (src, row_begin, visible pairs per (b, h))
+        self.steps = []
+        qp = self.pos[0]
+        for s in range(N):
+            src = (-s) % N
+            rb, _ = cp.cpattn_step_rows(self.maps[0], self.maps[src])
+            kp = self.pos[src]
+            pairs = _pairs_fast(qp, kp)
+            self.steps.append((src, rb, pairs))
+        self.pairs = sum(p for _, _, p in self.steps)
+        self.bh = w.B * w.H
+
+    def build_plan(self, do_bwd=True):
+        """Marshal every launch of one step once: (name, work, fn, args). The calls are the
+        library's C entry points with the same arguments the binding would pass."""
+        cp, w = self.cp, self.w
+        lib = cp.load()
+        T = cp._tensor
+        st = cp._stream(None)
+        bf16 = cp._dtype(self.q)
+        B, H, Tl, D, Tk = w.B, w.H, w.local_len, w.D, w.local_len
+        q, do = T(self.q), T(self.do)
+        o, lse, ob, lb = T(self.o), T(self.lse, 3), T(self.o_blk), T(self.l_blk, 3)
+        delta, dq = T(self.delta, 3), T(self.dq)
+        qm = cp._map(self.maps[0])
+        rope = (None, 0) if self.tab is None else (cp.ctypes.c_void_p(self.tab.data_ptr()), self.tab.shape[0])
+        by = cp.ctypes.byref
+        keep = [q, do, o, lse, ob, lb, delta, dq, qm]
+        plan = []
+        for s, (src, rb, pairs) in enumerate(self.steps):
+            if rb >= Tl:
+                continue
+            k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
+            keep += [k, v, km]
+            oo, ll = (o, lse) if s == 0 else (ob, lb)
+            plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd,
+                         (by(q), by(k), by(v), bf16, B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, rope[0], rope[1],
+                          0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
+            if s > 0:
+                plan.append(("lse_merge", (Tl - rb) * self.bh * (12 * D + 12), lib.cpattn_lse_merge,
+                             (by(o), by(lse), by(ob), by(lb), B, H, Tl, D, rb, Tl, st)))
+        if do_bwd:
+            plan.append(("bwd_preprocess", self.bh * Tl * (D * 2 + D * 4 + 4), lib.cpattn_bwd_preprocess,
+                         (by(do), bf16, by(o), by(delta), B, H, Tl, D, st)))
+            for src, rb, pairs in self.steps:
+                if rb >= Tl:
+                    continue
+                k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
+                dk, dv = T(self.dk[src]), T(self.dv[src])
+                keep += [k, v, km, dk, dv]
+                plan.append(("block_bwd_dkdv", 8 * D * pairs * self.bh, lib.cpattn_block_bwd_dkdv,
+                             (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dk), by(dv), B, H, Tl, Tk, D,
+                              by(qm), by(km), 1, 0.0, st)))
+                plan.append(("block_bwd_dq", 6 * D * pairs * self.bh, lib.cpattn_block_bwd_dq,
+                             (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), B, H, Tl, Tk, D, by(qm),
+                              by(km), 1, 0.0, st)))
+        self._keep = keep
+        self.plan = plan
+        self.do_bwd = do_bwd
+
+    def step(self, ev=None):
+        """One pass of the hot path. ``ev(name, work)`` returns a context that brackets one launch."""
+        rec = ev if ev is not None else _no_event
+        if self.do_bwd:
+            self.dq.zero_()
+            for x in self.dk + self.dv:
+                x.zero_()
+        for name, work, fn, args in self.plan:
+            with rec(name, work):
+                status = fn(*args)
+            if status != 0:
+                self.cp._check(status)
+
+    def flops(self, bwd=True):
+        return (4 + (10 if bwd else 0)) * self.w.D * self.pairs * self.bh
+
+
+def _pairs_fast(qp, kp):
+    import numpy as np
+    ks = np.sort(np.asarray(kp))
+    return int(np.searchsorted(ks, np.asarray(qp), side="right").sum())
+
+
+class _no_event:
+    def __init__(self, *a):
+        pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        return False
+
+
+class EventLog:
+    """HIP events around each launch on torch's current stream (the library's stream)."""
+
+    BOUND = {"block_fwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma", "lse_merge": "hbm",
+             "bwd_preprocess": "hbm"}
+
+    def __init__(self):
+        self.rec = []
+
+    def __call__(self, name, work):
+        import torch
+        log = self
+
+        class _C:
+            def __enter__(self_):
+                self_.a = torch.cuda.Event(enable_timing=True)
+                self_.b = torch.cuda.Event(enable_timing=True)
+                self_.a.record()
+                return self_
+
+            def __exit__(self_, *exc):
+                self_.b.record()
+                log.rec.append((name, work, self_.a, self_.b))
+                return False
+
+        return _C()
+
+    def summary(self):
+        out = {}
+        for name, work, a, b in self.rec:
+            d = out.setdefault(name, {"launches": 0, "ms": 0.0, "work": 0.0})
+            d["launches"] += 1
+            d["ms"] += a.elapsed_time(b)
+            d["work"] += work
+        res = {}
+        for name, d in out.items():
+            bound = self.BOUND[name]
+            sec = d["ms"] / 1e3
+            if bound == "mfma":
+                ach, unit, peak = d["work"] / sec / 1e12, "TFLOP/s", PEAK_BF16_TFLOPS
+            else:
+                ach, unit, peak = d["work"] / sec / 1e9, "GB/s", PEAK_HBM_GBS
+            res[name] = {"bound": bound, "launches": d["launches"], "avg_us": 1e3 * d["ms"] / d["launches"],
+                         "total_ms": d["ms"], "achieved": ach, "unit": unit, "peak": peak, "frac": ach / peak,
+                         "work_per_launch": d["work"] / d["launches"]}
+        return res
+
+
+def time_steps(share, steps, warmup, do_bwd=True, graph=True):
+    """Wall-clock time per step over ``steps`` steps (HIP-graph replays of one captured step when
+    ``graph``; each replay is checked bitwise against the eager result first), then per-launch HIP
+    event durations over ``steps`` eager steps queued behind a spin kernel so that the GPU never
+    waits for the host between launches."""
+    import torch
+    share.build_plan(do_bwd)
+    for _ in range(warmup):
+        share.step()
+    torch.cuda.synchronize()
+    outs = [share.o, share.lse] + ([share.dq] + share.dk + share.dv if do_bwd else [])
+    ref = [x.clone() for x in outs]
+    g = None
+    if graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                share.build_plan(do_bwd)  # launches must name the capture stream
+                share.step()
+            for _ in range(2):
+                for x in outs:
+                    x.fill_(float("nan"))
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                if not all(torch.equal(a, b) for a, b in zip(outs, ref)):
+                    raise RuntimeError("graph replay differs from the eager step")
+        except Exception as e:  # capture unsupported: time the eager loop
+            print(f"[bench] graph capture not used: {e}", file=sys.stderr)
+            g = None
+        share.build_plan(do_bwd)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if g is not None:
+            g.replay()
+        else:
+            share.step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ev = EventLog()
+    try:
+        torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the evented steps
+    except Exception:
+        pass
+    for _ in range(steps):
+        share.step(ev=ev)
+    torch.cuda.synchronize()
+    return wall, ev.summary(), g is not None
+
+
+def merge_hbm_probe(reps=20):
+    """The merge at the 16k-window shape (131072 rows, D=128: 202.9 MB) with the 256 MB
+    last-level cache flushed (512 MB written) before each timed launch."""
+    import torch
+
+    import context_causal_attention_cpattn_amd as cp
+    dev = torch.device("cuda:0")
+    B, H, T, D = 1, 32, 8192, 128
+    rb = 4096
+    g = torch.Generator(device=dev).manual_seed(5)
+    o_acc = torch.randn(B, H, T, D, device=dev, generator=g)
+    o_blk = torch.randn(B, H, T, D, device=dev, generator=g)
+    l_acc = torch.randn(B, H, T, device=dev, generator=g)
+    l_blk = torch.randn(B, H, T, device=dev, generator=g)
+    flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+    nbytes = B * H * (T - rb) * (12 * D + 12)
+    times = []
+    for i in range(reps + 3):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        cp.cpattn_lse_merge(o_acc, l_acc, o_blk, l_blk, rb, T)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 3:
+            times.append(a.elapsed_time(b))
+    times.sort()
+    med = times[len(times) // 2]
+    return {"rows": B * H * (T - rb), "bytes": nbytes, "median_us": med * 1e3,
+            "GB/s": nbytes / (med / 1e3) / 1e9, "frac_hbm": nbytes / (med / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "note": "512 MB written before each launch to evict the 256 MB last-level cache"}
+
+
+def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
+    """fp64 oracle on rank 0's whole share of the workload (every head, forward and backward),
+    repeated until at least ``min_seconds`` of host time have passed; reports the mean rate."""
+    import numpy as np
+
+    from oracle import attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t = share.host
+    f64 = lambda x: x.double().numpy()
+    q, k, v, do = f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"])
+    rows = list(share.pos[0])
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        O, L = oa.causal_attention_fwd(q, k, v, rows=rows)
+        oa.block_attention_bwd(q[:, :, rows], k, v, do[:, :, rows], O, L, rows, np.arange(w.T))
+        reps += 1
+    sec = (time.perf_counter() - t0) / reps
+    flops = share.flops()
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rank 0 share of {w.name}, all {w.B * w.H} heads, forward + backward in fp64 numpy, "
+                      f"{reps} repetition(s), {sec:.2f} s each", "seconds_per_step": sec}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    from workloads import BY_NAME
+    w = BY_NAME[args.workload]
+    share = Share(w, seed_do=w.seed + 1000)
+    wall, kern, graphed = time_steps(share, args.steps, args.warmup)
+    flops = share.flops()
+    value = flops / wall / 1e12
+    dom = max(kern, key=lambda n: kern[n]["total_ms"])
+    kd = kern[dom]
+    traffic = None
+    try:
+        tj = json.load(open(args.traffic))
+        if tj.get("kernel") == dom and tj.get("workload") == w.name:
+            traffic = tj.get("bytes_per_launch")
+    except Exception:
+        pass
+    line = {
+        "metric": "ring-block attention TFLOP/s per GPU (causal-effective) + % bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "graph_replay": graphed,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: rank 0 share of causal ring attention, HeadTail, B={w.B} H={w.H} "
+                               f"D={w.D} T={w.T} ring={w.ring}, forward (block fwd + LSE merge) and backward "
+                               f"(preprocess + dK/dV + dQ), all KV blocks resident",
+                   "B": w.B, "H": w.H, "D": w.D, "T": w.T, "ring": w.ring, "rank": 0,
+                   "causal_pairs_per_head": share.pairs, "flops_per_step": flops,
+                   "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"kernel": dom, "bound": kd["bound"], "achieved": round(kd["achieved"], 2),
+                     "peak": kd["peak"], "unit": kd["unit"], "frac": round(kd["frac"], 4), "traffic": traffic,
+                     "avg_launch_us": round(kd["avg_us"], 2), "work_per_launch": kd["work_per_launch"]},
+        "kernels": {n: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
+                    for n, d in kern.items()},
+    }
+    if not args.no_extra:
+        extra = {}
+        for name in ("win16k", "win32k"):
+            wx = BY_NAME[name]
+            sx = Share(wx, seed_do=wx.seed + 1000)
+            bwd = name == "win16k"
+            wl, kx, _ = time_steps(sx, 3, 1, do_bwd=bwd)
+            fl = sx.flops(bwd)
+            extra[name] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
+                           "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
+                           "parts": "forward + backward" if bwd else "forward with rotary",
+                           "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
+                                           "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
+            del sx
+            torch.cuda.empty_cache()
+        extra["merge_hbm_16k"] = merge_hbm_probe()
+        line["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, share)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

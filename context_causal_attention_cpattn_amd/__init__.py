@@ -22,7 +22,8 @@ from typing import Sequence
 __all__ = [
     "CpattnError", "lib_path", "load", "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard",
     "cpattn_rope_table", "cpattn_block_fwd", "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes",
-    "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "EXPORTS",
+    "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
+    "cpattn_step_rows", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +34,7 @@ CPATTN_F32, CPATTN_BF16 = 0, 1
 EXPORTS = (
     "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
-    "cpattn_block_bwd",
+    "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows",
 )
 
 
@@ -63,12 +64,17 @@ _SIGS = {
     "cpattn_block_fwd": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32, _f32, _vp,
                                         _i64, _i64, _i64, _T, _T, _vp]),
     "cpattn_lse_merge": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "cpattn_step_rows": (ctypes.c_int, [_M, _M, _i32, _P(_i64), _P(_i64)]),
     "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
     "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
     "cpattn_bwd_preprocess": (ctypes.c_int, [_T, _i32, _T, _T, _i64, _i64, _i64, _i64, _vp]),
     "cpattn_block_bwd": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M,
                                         _M, _i32, _f32, _vp]),
+    "cpattn_block_bwd_dkdv": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M,
+                                             _M, _i32, _f32, _vp]),
+    "cpattn_block_bwd_dq": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M, _M,
+                                           _i32, _f32, _vp]),
 }
 
 _lib = None
@@ -175,6 +181,13 @@ def cpattn_lse_merge(o_acc, lse_acc, o_blk, lse_blk, row_begin: int = 0, row_end
                                    D, row_begin, T if row_end is None else row_end, _stream(stream)))
 
 
+def cpattn_step_rows(qmap, kmap, causal: bool = True):
+    """(row_begin, visible_keys): local rows [row_begin, len) see keys [0, visible_keys) of the block."""
+    rb, nk = ctypes.c_int64(), ctypes.c_int64()
+    _check(load().cpattn_step_rows(_map(qmap), _map(kmap), int(causal), ctypes.byref(rb), ctypes.byref(nk)))
+    return rb.value, nk.value
+
+
 def cpattn_ring_fwd_workspace_bytes(B: int, H: int, Tq: int, D: int) -> int:
     return int(load().cpattn_ring_fwd_workspace_bytes(B, H, Tq, D))
 
@@ -211,3 +224,21 @@ def cpattn_block_bwd(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, km
     _check(load().cpattn_block_bwd(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                    _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq, Tk,
                                    D, _map(qmap), _map(kmap), int(causal), float(scale), _stream(stream)))
+
+
+def cpattn_block_bwd_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
+                          scale: float = 0.0, stream=None):
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    _check(load().cpattn_block_bwd_dkdv(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q),
+                                        _tensor(lse, 3), _tensor(delta, 3), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq,
+                                        Tk, D, _map(qmap), _map(kmap), int(causal), float(scale), _stream(stream)))
+
+
+def cpattn_block_bwd_dq(q, k, v, dout, lse, delta, dq_acc, qmap, kmap, causal: bool = True, scale: float = 0.0,
+                        stream=None):
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    _check(load().cpattn_block_bwd_dq(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
+                                      _tensor(delta, 3), _tensor(dq_acc), B, H, Tq, Tk, D, _map(qmap), _map(kmap),
+                                      int(causal), float(scale), _stream(stream)))

@@ -356,21 +356,26 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
 }
 
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;
-  hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
-  return hipGetLastError();
+  if (which & 1) {
+    hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (which & 2) {
+    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
-  return a.D == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int which, hipStream_t s) {
+  return a.D == 64 ? launch_d<64>(a, which, s) : launch_d<128>(a, which, s);
 }
 
 }  // namespace cpattn

@@ -197,6 +197,24 @@ int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, c
   return launch_status(launch_merge(m, (hipStream_t)stream), "lse_merge");
 }
 
+int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, int64_t* row_begin,
+                     int64_t* visible_keys) {
+  if (!qmap || !kmap || !row_begin || !visible_keys) return fail(CPATTN_EINVAL, "null argument");
+  int st;
+  if (qmap->len <= 0 || kmap->len <= 0) return fail(CPATTN_EINVAL, "maps must be non-empty");
+  if ((st = check_map(qmap, qmap->len, "qmap")) || (st = check_map(kmap, kmap->len, "kmap"))) return st;
+  if (!causal) {
+    *row_begin = 0;
+    *visible_keys = kmap->len;
+    return ok();
+  }
+  const PosMap qm = to_map(qmap), km = to_map(kmap);
+  // rows whose position is below the block's first key position see nothing
+  *row_begin = qm.count_lt(km.pos(0));
+  *visible_keys = *row_begin < qmap->len ? km.count_le(qm.pos((int)qmap->len - 1)) : 0;
+  return ok();
+}
+
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D) {
   if (B <= 0 || H <= 0 || Tq <= 0 || D <= 0) return 0;
   const size_t o = (size_t)B * H * Tq * D * 4;
@@ -231,16 +249,11 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
   cpattn_tensor o_blk{o_ws, H * Tq * D, Tq * D, D};
   cpattn_tensor l_blk{l_ws, H * Tq, Tq, 1};
   hipStream_t s = (hipStream_t)stream;
-  const PosMap qm = to_map(qmap);
   for (int32_t step = 0; step < ring; ++step) {
     const int32_t src = ((rank - step) % ring + ring) % ring;
     const cpattn_posmap* km = &kmaps[src];
-    // rows that see at least one key of this block: positions >= the block's first key
-    int64_t rb = 0;
-    if (causal) {
-      const int64_t first_key_pos = km->len > 0 ? (km->split > 0 ? km->d0 : km->d1) : 0;
-      rb = qm.count_lt((int)first_key_pos);
-    }
+    int64_t rb = 0, nvis = 0;
+    if ((st = cpattn_step_rows(qmap, km, causal, &rb, &nvis))) return st;
     if (step == 0) {
       // step 0 fills every row of the accumulator (rows without a visible key get O = 0, LSE = -inf)
       FwdArgs a{};
@@ -286,33 +299,71 @@ int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn
   return launch_status(launch_bwd_preprocess(p, (hipStream_t)stream), "bwd_preprocess");
 }
 
-int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
-                     const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
-                     const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
-                     int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
-                     const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, const cpattn_tensor* dout,
+               int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
+               const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq,
+               int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+               float scale, int which, void* stream, const char* what) {
   int st;
   if ((st = check_dims(B, H, Tq, Tk, D))) return st;
   if (dtype == CPATTN_F32) return fail(CPATTN_EUNSUPPORTED, "block backward takes bf16 inputs");
   if (dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d", (int)dtype);
   if ((st = check_tensor(q, "q", 2)) || (st = check_tensor(k, "k", 2)) || (st = check_tensor(v, "v", 2)) ||
-      (st = check_tensor(dout, "dout", 2)) || (st = check_rows(lse, "lse")) || (st = check_rows(delta, "delta")) ||
-      (st = check_tensor(dq_acc, "dq_acc", 4)) || (st = check_tensor(dk_acc, "dk_acc", 4)) ||
-      (st = check_tensor(dv_acc, "dv_acc", 4)))
+      (st = check_tensor(dout, "dout", 2)) || (st = check_rows(lse, "lse")) || (st = check_rows(delta, "delta")))
+    return st;
+  if ((which & 2) && (st = check_tensor(dq_acc, "dq_acc", 4))) return st;
+  if ((which & 1) && ((st = check_tensor(dk_acc, "dk_acc", 4)) || (st = check_tensor(dv_acc, "dv_acc", 4))))
     return st;
   if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
   if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
   BwdArgs a{};
   a.q = view(q), a.k = view(k), a.v = view(v), a.dout = view(dout);
   a.lse = view(lse), a.delta = view(delta);
-  a.dq = (float*)dq_acc->data, a.dq_sb = dq_acc->sb, a.dq_sh = dq_acc->sh, a.dq_st = dq_acc->st;
-  a.dk = (float*)dk_acc->data, a.dk_sb = dk_acc->sb, a.dk_sh = dk_acc->sh, a.dk_st = dk_acc->st;
-  a.dv = (float*)dv_acc->data, a.dv_sb = dv_acc->sb, a.dv_sh = dv_acc->sh, a.dv_st = dv_acc->st;
+  if (which & 2) a.dq = (float*)dq_acc->data, a.dq_sb = dq_acc->sb, a.dq_sh = dq_acc->sh, a.dq_st = dq_acc->st;
+  if (which & 1) {
+    a.dk = (float*)dk_acc->data, a.dk_sb = dk_acc->sb, a.dk_sh = dk_acc->sh, a.dk_st = dk_acc->st;
+    a.dv = (float*)dv_acc->data, a.dv_sb = dv_acc->sb, a.dv_sh = dv_acc->sh, a.dv_st = dv_acc->st;
+  }
   a.B = (int)B, a.H = (int)H, a.Tq = (int)Tq, a.Tk = (int)Tk, a.D = (int)D;
   a.qm = to_map(qmap), a.km = to_map(kmap);
   a.causal = causal != 0;
   a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
-  return launch_status(launch_bwd_bf16(a, (hipStream_t)stream), "block_bwd");
+  return launch_status(launch_bwd_bf16(a, which, (hipStream_t)stream), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                     const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
+                     const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
+                     int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+                     const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+  return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
+                    scale, 3, stream, "block_bwd");
+}
+
+int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                          const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                          const cpattn_tensor* delta, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
+                          int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+                          const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+  return bwd_common(q, k, v, dout, dtype, lse, delta, nullptr, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
+                    scale, 1, stream, "block_bwd_dkdv");
+}
+
+int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                        const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
+                        const cpattn_tensor* dq_acc, int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
+                        const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
+                        void* stream) {
+  return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, nullptr, nullptr, B, H, Tq, Tk, D, qmap, kmap, causal,
+                    scale, 2, stream, "block_bwd_dq");
 }
 
 }  // extern "C"

@@ -69,7 +69,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PreArgs& a, hipStream_t s);
-hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+// which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both
+hipError_t launch_bwd_bf16(const BwdArgs& a, int which, hipStream_t s);
 hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStream_t s);
 
 }  // namespace cpattn

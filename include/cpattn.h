@@ -141,6 +141,23 @@ int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc,
                      int64_t B, int64_t H, int64_t T, int64_t D,
                      int64_t row_begin, int64_t row_end, void* stream);
 
+/*
+ * Step classification (host only, integer, exact): the local query rows that
+ * see at least one key of a KV block. Positions increase with the local
+ * index, so they form the suffix [*row_begin, qmap->len); *visible_keys is the
+ * number of keys any of them can see (a prefix of the block). With causal = 0
+ * every row sees every key. Under HeadTail this yields the three step shapes
+ * of the BluScriptCP log (2026-06-17): the causal diagonal for the own block,
+ * all rows against the head half of the keys for an earlier rank's block, and
+ * the tail half of the rows against all keys for a later rank's block.
+ * A caller that receives blocks one at a time (a real ring) drives each step
+ * with cpattn_block_fwd on rows [*row_begin, len) and cpattn_lse_merge, which
+ * is what cpattn_ring_fwd does with resident blocks.
+ * Errors: EINVAL for null pointers or an invalid map.
+ */
+int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                     int64_t* row_begin, int64_t* visible_keys);
+
 /* Workspace bytes cpattn_ring_fwd needs: an fp32 block output and LSE. */
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D);
 
@@ -198,6 +215,28 @@ int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
                      int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
                      const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
                      float scale, void* stream);
+
+/*
+ * The two halves of cpattn_block_bwd, same arguments and accumulate semantics:
+ * _dkdv adds into dk_acc and dv_acc only (key-tile-major kernel), _dq adds
+ * into dq_acc only (query-tile-major kernel). In a real ring the dK/dV
+ * partials travel back to their owner while dQ stays local (BluScriptCP log,
+ * 2026-03-21 and 2026-06-22 on the dK/dV accumulator that rotates with its
+ * block), so launching _dkdv first lets that transfer overlap with _dq.
+ * Arguments that a half does not use may be NULL (dq_acc for _dkdv; dk_acc
+ * and dv_acc for _dq).
+ */
+int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                          const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                          const cpattn_tensor* delta, const cpattn_tensor* dk_acc,
+                          const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
+                          int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap,
+                          int32_t causal, float scale, void* stream);
+int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                        const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                        const cpattn_tensor* delta, const cpattn_tensor* dq_acc, int64_t B, int64_t H,
+                        int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
+                        const cpattn_posmap* kmap, int32_t causal, float scale, void* stream);
 
 #ifdef __cplusplus
 }

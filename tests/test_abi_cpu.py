@@ -138,3 +138,36 @@ def test_rope_table_rejects():
     assert lib.cpattn_rope_table(0.0, 10, 128, ctypes.c_void_p(0x1000), None) == -1
     assert lib.cpattn_rope_table(10000.0, 10, 127, ctypes.c_void_p(0x1000), None) == -1
     assert lib.cpattn_rope_table(10000.0, 10, 128, None, None) == -1
+
+
+@pytest.mark.parametrize("T,ring", [(256, 2), (4096, 4), (48, 3), (16384, 2)])
+def test_step_rows_matches_positions(T, ring):
+    # rows that see a key of the block, and the keys any of them can see, from explicit positions
+    c = T // (2 * ring)
+    for r in range(ring):
+        qmap, qpos = cp.cpattn_headtail_shard(T, ring, r)
+        assert qpos == shard.headtail_positions(T, ring, r)
+        for src in range(ring):
+            kmap, _ = cp.cpattn_headtail_shard(T, ring, src)
+            kpos = shard.headtail_positions(T, ring, src)
+            rb, nk = cp.cpattn_step_rows(qmap, kmap)
+            seen = [i for i, p in enumerate(qpos) if min(kpos) <= p]
+            assert rb == (seen[0] if seen else len(qpos))
+            assert nk == sum(1 for kp in kpos if kp <= max(qpos))
+            # the three HeadTail step shapes
+            if src == r:
+                assert (rb, nk) == (0, 2 * c)
+            elif src < r:
+                assert (rb, nk) == (0, c)
+            else:
+                assert (rb, nk) == (c, 2 * c)
+            assert cp.cpattn_step_rows(qmap, kmap, causal=False) == (0, 2 * c)
+
+
+def test_step_rows_rejects():
+    lib = cp.load()
+    rb, nk = ctypes.c_int64(), ctypes.c_int64()
+    good = cp.cpattn_posmap(8, 4, 0, 4)
+    bad = cp.cpattn_posmap(8, 4, 4, 0)
+    assert lib.cpattn_step_rows(ctypes.byref(good), ctypes.byref(bad), 1, ctypes.byref(rb), ctypes.byref(nk)) == -1
+    assert lib.cpattn_step_rows(None, ctypes.byref(good), 1, ctypes.byref(rb), ctypes.byref(nk)) == -1

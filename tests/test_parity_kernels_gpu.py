@@ -278,3 +278,47 @@ def test_determinism_bitwise():
     b = run_ring_bwd(q, k, v, do, 2)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_split_backward_and_step_driven_forward_match_bitwise():
+    # cpattn_block_bwd == cpattn_block_bwd_dkdv + cpattn_block_bwd_dq, and a caller driving the ring
+    # step by step (cpattn_step_rows + cpattn_block_fwd + cpattn_lse_merge) == cpattn_ring_fwd.
+    log("split backward / step-driven forward")
+    B, H, T, D, N = 2, 3, 768, 64, 3
+    q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=77, n=4)
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, r) for r in range(N)])
+    Tl = T // N
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    r = 1
+    qr, dor = gather(q, pos[r]), gather(do, pos[r])
+    ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(B, H, Tl, D), dtype=torch.uint8, device=DEV)
+    o1 = torch.empty(B, H, Tl, D, device=DEV)
+    l1 = torch.empty(B, H, Tl, device=DEV)
+    cp.cpattn_ring_fwd(qr, kb, vb, maps, r, maps[r], o1, l1, ws)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    ob = torch.empty_like(o1)
+    lb = torch.empty_like(l1)
+    for s in range(N):
+        src = (r - s) % N
+        rb, _ = cp.cpattn_step_rows(maps[r], maps[src])
+        if s == 0:
+            cp.cpattn_block_fwd(qr, kb[src], vb[src], maps[r], maps[src], o2, l2)
+        elif rb < Tl:
+            cp.cpattn_block_fwd(qr, kb[src], vb[src], maps[r], maps[src], ob, lb, row_begin=rb)
+            cp.cpattn_lse_merge(o2, l2, ob, lb, rb, Tl)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    delta = torch.empty(B, H, Tl, device=DEV)
+    cp.cpattn_bwd_preprocess(dor, o1, delta)
+    acc = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(6)]
+    for s in range(N):
+        src = (r - s) % N
+        cp.cpattn_block_bwd(qr, kb[src], vb[src], dor, l1, delta, acc[0], acc[1], acc[2], maps[r], maps[src])
+        cp.cpattn_block_bwd_dkdv(qr, kb[src], vb[src], dor, l1, delta, acc[4], acc[5], maps[r], maps[src])
+        cp.cpattn_block_bwd_dq(qr, kb[src], vb[src], dor, l1, delta, acc[3], maps[r], maps[src])
+    torch.cuda.synchronize()
+    for a_, b_ in zip(acc[:3], acc[3:]):
+        assert torch.equal(a_, b_)
+    assert acc[0].abs().sum() > 0
