@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--workload", default="gpt2s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
+    ap.add_argument("--no-graph", action="store_true", help="time eager steps instead of graph replays")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch of the dominant kernel (from rocprofv3 --pmc)")
     return ap.parse_args()
@@ -349,7 +350,7 @@ def main():
     from workloads import BY_NAME
     w = BY_NAME[args.workload]
     share = Share(w, seed_do=w.seed + 1000)
-    wall, kern, graphed = time_steps(share, args.steps, args.warmup)
+    wall, kern, graphed = time_steps(share, args.steps, args.warmup, graph=not args.no_graph)
     flops = share.flops()
     value = flops / wall / 1e12
     dom = max(kern, key=lambda n: kern[n]["total_ms"])

@@ -17,6 +17,8 @@
 //   * dq: a workgroup owns 128 query rows and walks the visible key tiles, like
 //     the forward: S^T = K Q^T and dP^T = V dO^T give one query per lane, and
 //     dQ^T += K^T dS^T reads K^T with the transposing LDS read.
+// Tiles are staged through LDS with direct global->LDS loads into the
+// swizzled, unpadded layout of common.h (double buffered, one barrier per tile).
 
 #include "internal.h"
 
@@ -24,33 +26,62 @@ namespace cpattn {
 namespace {
 
 constexpr int kNW = 4;
-constexpr int kPad = 8;
+constexpr int kTile = 64;  // rows of the streamed tile (queries for dkdv, keys for dq)
 
 template <int D>
 struct BCfg {
-  static constexpr int LDP = D + kPad;
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILEB = kTile * ROWB;
+  static constexpr int NI = kTile * CPR / (64 * kNW);  // direct loads per wave per tile
   static constexpr int NC = D / 16;
   static constexpr int NDB = D / 32;
 };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
+// Per-lane byte offsets into a swizzled tile.
+//   row-operand reads (b128): row 32*blk + lq, logical chunk 2c + h  -> base + 32*blk*ROWB + ro[c]
+//   transposing reads (b64):  rows 16t + 4h + (l%16)/4 (+8 for hi), columns 32db + 16((l/16)%2) + 4(l%4)
+//                             -> base + 16*t*ROWB + tro[hi][db]
+template <int D>
+struct Offs {
+  int ro[D / 16];
+  int tro[2][D / 32];
+  __device__ __forceinline__ Offs(int l) {
+    using C = BCfg<D>;
+    const int h = l >> 5, lq = l & 31;
+    const int m = swz_mask<D>(lq);
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) ro[c] = lq * C::ROWB + (((2 * c + h) ^ m) * 16);
+    const int r0 = 4 * h + ((l & 15) >> 2);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = r0 + 8 * hi;
+      const int mm = swz_mask<D>(r);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int cc = 4 * db + 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+        tro[hi][db] = r * C::ROWB + ((cc ^ mm) * 16) + (l & 1) * 8;
+      }
+    }
+  }
+};
+
 // ------------------------------------------------------------------ dK / dV
 constexpr int kKeysPerWG = 32 * kNW;  // 128
-constexpr int kQTile = 64;
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   using C = BCfg<D>;
-  constexpr int TILE = kQTile * C::LDP;
-  constexpr int CH = kQTile * D / 8 / (64 * kNW);  // 16-byte chunks per thread per tensor
-  __shared__ __attribute__((aligned(16))) __bf16 sq[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sdo[2][TILE];
-  __shared__ __attribute__((aligned(16))) float slse[2][kQTile];
-  __shared__ __attribute__((aligned(16))) float sdelta[2][kQTile];
+  __shared__ __attribute__((aligned(1024))) char sq[2][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sdo[2][C::TILEB];
+  __shared__ __attribute__((aligned(16))) float slse[2][kTile];
+  __shared__ __attribute__((aligned(16))) float sdelta[2][kTile];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, h = l >> 5, lq = l & 31;
   const int Lg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = Lg / n_kt;
   const int kt = Lg - bh * n_kt;
@@ -77,33 +108,49 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
       vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
     }
   }
-  const int kpos = a.km.pos(key_ok ? key : a.Tk - 1);
+  // complete the register loads before the tile loop (see the forward kernel)
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
+  // Positions increase with the local index, so the query rows that see this lane's key
+  // are [qlo, Tq); the wave's last key has the largest qlo.
+  const int qlo = a.causal ? a.qm.count_lt(a.km.pos(key_ok ? key : a.Tk - 1)) : 0;
   const int wave_last_key = (kw0 + 31 < a.Tk ? kw0 + 31 : a.Tk - 1);
-  const int wave_max_kpos = a.km.pos(wave_last_key < 0 ? 0 : wave_last_key);
+  const int wave_qlo = a.causal ? a.qm.count_lt(a.km.pos(wave_last_key)) : 0;
 
   // query rows that can see a key of this workgroup
   const int q_first = a.causal ? a.qm.count_lt(a.km.pos(kc0)) : 0;
-  const int t_begin = q_first / kQTile;
-  const int t_end = (a.Tq + kQTile - 1) / kQTile;
+  const int t_begin = q_first / kTile;
+  const int t_end = (a.Tq + kTile - 1) / kTile;
   const float sl2 = a.scale * kLog2e;
 
-  u32x4 rq[CH], rdo[CH];
-  float rl = 0.f, rd = 0.f;
-  auto load_tile = [&](int t) {
-    const int q0 = t * kQTile;
+  int ld_row[C::NI], ld_col[C::NI];
+  unsigned qo[C::NI], oo[C::NI];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 64 * kNW * i;
-      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-      const int qrow = q0 + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      rq[i] = rdo[i] = z;
-      if (qrow < a.Tq) {
-        rq[i] = ldg16(qp + (int64_t)qrow * a.q.st + cc);
-        rdo[i] = ldg16(dop + (int64_t)qrow * a.dout.st + cc);
+  for (int i = 0; i < C::NI; ++i) {
+    const int p = (w * C::NI + i) * 64 + l;
+    ld_row[i] = p / C::CPR;
+    ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
+    qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
+    oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
+  }
+  float rl = 0.f, rd = 0.f;
+  auto issue_tile = [&](int t, int buf) {
+    const int q0 = t * kTile;
+    const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
+    const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
+    const bool tail = q0 + kTile > a.Tq;  // rows past the end repeat the last row (masked)
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      unsigned q_off = qo[i], o_off = oo[i];
+      if (tail) {
+        const int r = min(ld_row[i], a.Tq - 1 - q0);
+        q_off = (unsigned)((r * a.q.st + ld_col[i]) * 2);
+        o_off = (unsigned)((r * a.dout.st + ld_col[i]) * 2);
       }
+      load_lds16(qbase, q_off, sq[buf] + (w * C::NI + i) * 1024);
+      load_lds16(obase, o_off, sdo[buf] + (w * C::NI + i) * 1024);
     }
-    if (tid < kQTile) {
+    if (tid < kTile) {
       const int qrow = q0 + tid;
       rl = INFINITY;  // rows past the end (or without any visible key) give P = 0
       rd = 0.f;
@@ -114,47 +161,39 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
       }
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 64 * kNW * i;
-      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-      *(u32x4*)(sq[buf] + r * C::LDP + cc) = rq[i];
-      *(u32x4*)(sdo[buf] + r * C::LDP + cc) = rdo[i];
-    }
-    if (tid < kQTile) {
+  auto store_rows = [&](int buf) {
+    if (tid < kTile) {
       slse[buf][tid] = rl;
       sdelta[buf][tid] = rd;
     }
   };
 
+  const Offs<D> off(l);
   f32x16 dk[C::NDB], dv[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = f32x16{};
 
   if (t_begin < t_end) {
-    load_tile(t_begin);
-    store_tile(0);
+    issue_tile(t_begin, 0);
+    store_rows(0);
   }
-  __syncthreads();
 
   for (int t = t_begin; t < t_end; ++t) {
     const int cur = (t - t_begin) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);
-    const __bf16* Q = sq[cur];
-    const __bf16* DO = sdo[cur];
-    const int q0 = t * kQTile;
-    const bool full = (q0 + kQTile <= a.Tq) && (key_ok && kw0 + 31 < a.Tk) &&
-                      (!a.causal || a.qm.pos(q0) >= wave_max_kpos);
+    wait_vm0();
+    __syncthreads();
+    if (t + 1 < t_end) issue_tile(t + 1, cur ^ 1);
+    const char* Q = sq[cur];
+    const char* DO = sdo[cur];
+    const int q0 = t * kTile;
+    const bool full = (q0 + kTile <= a.Tq) && (kw0 + 31 < a.Tk) && (q0 >= wave_qlo);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 s = f32x16{}, dpv = f32x16{};
-      const __bf16* qa = Q + (32 * qb + lq) * C::LDP + 8 * h;
-      const __bf16* da = DO + (32 * qb + lq) * C::LDP + 8 * h;
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        s = mfma32(*(const bf16x8*)(qa + 16 * c), kf[c], s);
-        dpv = mfma32(*(const bf16x8*)(da + 16 * c), vf[c], dpv);
+        s = mfma32(*(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]), kf[c], s);
+        dpv = mfma32(*(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]), vf[c], dpv);
       }
       // rows of s / dpv: query 32qb + 8g + 4h + j, column: this lane's key
       bf16x8 pa[2], dsa[2];
@@ -168,32 +207,32 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
           float p = fast_exp2(fmaf(s[r], sl2, -L4[j]));
           if (!full) {
             const int qrow = q0 + 32 * qb + 8 * g + 4 * h + j;
-            const bool vis = key_ok && qrow < a.Tq && (!a.causal || kpos <= a.qm.pos(qrow));
-            p = vis ? p : 0.f;
+            p = (key_ok && qrow >= qlo && qrow < a.Tq) ? p : 0.f;
           }
           const float ds = p * (dpv[r] - D4[j]);
           pa[r >> 3][r & 7] = (__bf16)p;
           dsa[r >> 3][r & 7] = (__bf16)ds;
         }
       }
-      // dV += P^T dO, dK += dS^T Q ; B operand rows = queries 16tt' + 4h + {0..3}, +8
+      // dV += P^T dO, dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const int rr = 32 * qb + 16 * tt + 4 * h + ((l & 15) >> 2);
+        const int rb = (32 * qb + 16 * tt) * C::ROWB;
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const int col = 32 * db + 16 * ((l >> 4) & 1) + 4 * (l & 3);
-          const bf16x8 ob = cat8(lds_read_tr4(DO + rr * C::LDP + col), lds_read_tr4(DO + (rr + 8) * C::LDP + col));
+          const bf16x8 ob = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
+                                 lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
           dv[db] = mfma32(pa[tt], ob, dv[db]);
-          const bf16x8 qbv = cat8(lds_read_tr4(Q + rr * C::LDP + col), lds_read_tr4(Q + (rr + 8) * C::LDP + col));
-          dk[db] = mfma32(dsa[tt], qbv, dk[db]);
+          const bf16x8 qv = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
+                                 lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
+          dk[db] = mfma32(dsa[tt], qv, dk[db]);
         }
       }
     }
-    if (t + 1 < t_end) store_tile(cur ^ 1);
-    __syncthreads();
+    if (t + 1 < t_end) store_rows(cur ^ 1);
   }
 
+  if (t_begin >= t_end) return;  // no query of this block sees these keys: nothing to add
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j
   float* dkp = a.dk + b * a.dk_sb + hh * a.dk_sh;
   float* dvp = a.dv + b * a.dv_sb + hh * a.dv_sh;
@@ -213,18 +252,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
 
 // ------------------------------------------------------------------ dQ
 constexpr int kQPerWG = 32 * kNW;  // 128
-constexpr int kKTile = 64;
 
 template <int D>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
   using C = BCfg<D>;
-  constexpr int TILE = kKTile * C::LDP;
-  constexpr int CH = kKTile * D / 8 / (64 * kNW);
-  __shared__ __attribute__((aligned(16))) __bf16 sk[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sv[2][TILE];
+  __shared__ __attribute__((aligned(1024))) char sk[2][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sv[2][C::TILEB];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, h = l >> 5, lq = l & 31;
   const int Lg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = Lg / n_qt;
   const int qt = n_qt - 1 - (Lg - bh * n_qt);
@@ -253,74 +290,79 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
     lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
     dl = ((const float*)a.delta.p)[b * a.delta.sb + hh * a.delta.sh + (int64_t)row * a.delta.st];
   }
+  // complete the register loads before the tile loop (see the forward kernel)
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]), "v"(df[c]));
+  asm volatile("" ::"v"(lse2), "v"(dl));
+
   const int qpos = a.qm.pos(row_ok ? row : a.Tq - 1);
   const int last_row = (q0 + kQPerWG < a.Tq ? q0 + kQPerWG : a.Tq) - 1;
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
-  const int n_kt = (n_vis + kKTile - 1) / kKTile;
+  const int n_kt = (n_vis + kTile - 1) / kTile;
+  // the keys this row sees are the prefix [0, lim) of the block (positions increase)
   const int wave_first = q0 + 32 * w < a.Tq ? q0 + 32 * w : a.Tq - 1;
-  const int wave_min_pos = a.qm.pos(wave_first);
+  const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
+  const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
   const float sl2 = a.scale * kLog2e;
 
-  u32x4 rk[CH], rv[CH];
-  auto load_tile = [&](int kt) {
+  int ld_row[C::NI], ld_col[C::NI];
+  unsigned ko[C::NI], vo[C::NI];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 64 * kNW * i;
-      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-      const int key = kt * kKTile + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      rk[i] = rv[i] = z;
-      if (key < a.Tk) {
-        rk[i] = ldg16(kp + (int64_t)key * a.k.st + cc);
-        rv[i] = ldg16(vp + (int64_t)key * a.v.st + cc);
+  for (int i = 0; i < C::NI; ++i) {
+    const int p = (w * C::NI + i) * 64 + l;
+    ld_row[i] = p / C::CPR;
+    ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
+    ko[i] = (unsigned)((ld_row[i] * a.k.st + ld_col[i]) * 2);
+    vo[i] = (unsigned)((ld_row[i] * a.v.st + ld_col[i]) * 2);
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const char* kbase = (const char*)(kp + (int64_t)kt * kTile * a.k.st);
+    const char* vbase = (const char*)(vp + (int64_t)kt * kTile * a.v.st);
+    const bool tail = kt * kTile + kTile > a.Tk;  // rows past the block repeat the last key (masked)
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      unsigned k_off = ko[i], v_off = vo[i];
+      if (tail) {
+        const int r = min(ld_row[i], a.Tk - 1 - kt * kTile);
+        k_off = (unsigned)((r * a.k.st + ld_col[i]) * 2);
+        v_off = (unsigned)((r * a.v.st + ld_col[i]) * 2);
       }
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + 64 * kNW * i;
-      const int r = c / (D / 8), cc = (c % (D / 8)) * 8;
-      *(u32x4*)(sk[buf] + r * C::LDP + cc) = rk[i];
-      *(u32x4*)(sv[buf] + r * C::LDP + cc) = rv[i];
+      load_lds16(kbase, k_off, sk[buf] + (w * C::NI + i) * 1024);
+      load_lds16(vbase, v_off, sv[buf] + (w * C::NI + i) * 1024);
     }
   };
 
+  const Offs<D> off(l);
   f32x16 acc[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
+  if (n_kt > 0) issue_tile(0, 0);
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const __bf16* K = sk[cur];
-    const __bf16* V = sv[cur];
-    const int k0 = kt * kKTile;
-    const bool full = (k0 + kKTile <= a.Tk) && (!a.causal || a.km.pos(k0 + kKTile - 1) <= wave_min_pos);
+    wait_vm0();
+    __syncthreads();
+    if (kt + 1 < n_kt) issue_tile(kt + 1, cur ^ 1);
+    const char* K = sk[cur];
+    const char* V = sv[cur];
+    const int k0 = kt * kTile;
+    const bool full = k0 + kTile <= wave_lim;
     bf16x8 dsb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16 s = f32x16{}, dpv = f32x16{};
-      const __bf16* ka = K + (32 * kb + lq) * C::LDP + 8 * h;
-      const __bf16* va = V + (32 * kb + lq) * C::LDP + 8 * h;
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        s = mfma32(*(const bf16x8*)(ka + 16 * c), qf[c], s);
-        dpv = mfma32(*(const bf16x8*)(va + 16 * c), df[c], dpv);
+        s = mfma32(*(const bf16x8*)(K + 32 * kb * C::ROWB + off.ro[c]), qf[c], s);
+        dpv = mfma32(*(const bf16x8*)(V + 32 * kb * C::ROWB + off.ro[c]), df[c], dpv);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(fmaf(s[r], sl2, -lse2));
         if (!full) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool vis = key < a.Tk && (!a.causal || a.km.pos(key) <= qpos);
-          p = vis ? p : 0.f;
+          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          p = kk < lim ? p : 0.f;
         }
         dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dpv[r] - dl));
       }
@@ -328,16 +370,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
     // dQ^T += K^T dS^T ; K^T operand rows = d, 8 keys 16t + 4h + {0..3}, +8
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int rr = 16 * t + 4 * h + ((l & 15) >> 2);
+      const int rb = 16 * t * C::ROWB;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const int col = 32 * db + 16 * ((l >> 4) & 1) + 4 * (l & 3);
-        const bf16x8 kt8 = cat8(lds_read_tr4(K + rr * C::LDP + col), lds_read_tr4(K + (rr + 8) * C::LDP + col));
+        const bf16x8 kt8 = cat8(lds_read_tr4((const __bf16*)(K + rb + off.tro[0][db])),
+                                lds_read_tr4((const __bf16*)(K + rb + off.tro[1][db])));
         acc[db] = mfma32(kt8, dsb[t], acc[db]);
       }
     }
-    if (kt + 1 < n_kt) store_tile(cur ^ 1);
-    __syncthreads();
   }
 
   if (row_ok) {

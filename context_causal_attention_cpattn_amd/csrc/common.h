@@ -59,6 +59,46 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// LDS tiles of 16-bit elements, D per row, stored without padding. The 16-byte
+// chunk c of row r sits at physical chunk c ^ swz_mask<D>(r). With 64 banks of
+// 4 bytes this is free of bank conflicts for (a) 16-byte reads where 16 lanes
+// take the same logical chunk of 16 consecutive rows and (b) transposing
+// 8-byte reads where 32 lanes take 4 consecutive rows x 32 bytes, and linear
+// 16-byte stores (lane i -> i-th chunk of the tile) stay conflict-free too.
+template <int D>
+__device__ __forceinline__ int swz_mask(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_wave_base +
+// 16 * lane (global_load_lds_dwordx4). Issued through inline assembly so that
+// the compiler adds no conservative wait before later LDS reads: each kernel
+// orders these writes itself (s_waitcnt vmcnt(0), then a barrier, before a
+// tile is read). Loads complete in issue order, so these extra loads can only
+// make the compiler's own vmcnt waits longer, never shorter. An SALU write of
+// M0 followed by an LDS-DMA instruction that reads M0 needs one wait state on
+// this architecture family; the compiler's hazard recognizer cannot see inside
+// the asm block, so the s_nop is written here.
+// `base` is wave-uniform (scalar registers); `off` is the lane's unsigned byte
+// offset from it.
+__device__ __forceinline__ void load_lds16(const void* base, unsigned off, const void* lds_wave_base) {
+  const unsigned lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// Sum of the 8 bf16 values of v, added to acc (v_dot2 against (1, 1)).
+__device__ __forceinline__ float sum8_bf16(const bf16x8& v, float acc) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2 * i], v[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workgroup id -> logical tile id so that consecutive logical tiles land on
 // the same XCD. Workgroups are dealt to the 8 XCDs round-robin by id, so XCD x
 // runs ids x, x+8, x+16, ...; logical tiles [x*per + min(x,rem), ...) go there.

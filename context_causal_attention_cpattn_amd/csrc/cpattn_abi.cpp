@@ -44,6 +44,8 @@ int check_tensor(const cpattn_tensor* t, const char* name, int esize) {
   if (t->sb % q || t->sh % q || t->st % q)
     return fail(CPATTN_EINVAL, "%s: B/H/T strides must be multiples of %lld elements", name, (long long)q);
   if (t->sb < 0 || t->sh < 0 || t->st < 0) return fail(CPATTN_EINVAL, "%s: negative stride", name);
+  // kernels address a 64-row tile with 32-bit byte offsets
+  if (t->st * 64 * esize >= (int64_t)1 << 31) return fail(CPATTN_EINVAL, "%s: T stride too large", name);
   return CPATTN_OK;
 }
 

@@ -9,10 +9,13 @@
 //
 // Work decomposition
 //   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
-//     rows for the whole kernel;
-//   * K and V tiles of 64 keys are staged through LDS, double buffered, loaded
-//     with coalesced 16-byte global loads;
-//   * scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16,
+//     rows for the whole kernel and keeps them in registers;
+//   * K and V tiles of 64 keys are staged through LDS, double buffered. They
+//     are loaded with global_load_lds_dwordx4 (16 bytes per lane straight into
+//     LDS, no register staging) into an unpadded, XOR-swizzled layout that is
+//     free of bank conflicts both for the 16-byte row reads of the K operand and
+//     for the transposing reads of the V^T operand;
+//   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
 //     so every lane holds 16 scores of ONE query row per 32-key block: the row
 //     max is an in-lane max3 chain plus one exchange with lane l^32, and the row
 //     sum stays a per-lane partial until the epilogue;
@@ -26,6 +29,9 @@
 //     (exact: O and the row sum always share the same reference max);
 //   * workgroup ids are remapped so that the query tiles of one (b, h) run on
 //     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first.
+//   * with rotary embedding, K is staged through registers instead (it must be
+//     rotated at its global position before it reaches LDS); Q is rotated once
+//     in the prologue.
 
 #include "internal.h"
 
@@ -35,18 +41,19 @@ namespace {
 constexpr int kNW = 4;          // waves per workgroup
 constexpr int kBM = 32 * kNW;   // query rows per workgroup
 constexpr int kBN = 64;         // keys per tile
-constexpr int kPad = 8;         // LDS row padding (elements)
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
 template <int D>
 struct Cfg {
-  static constexpr int LDP = D + kPad;             // LDS row pitch (elements)
-  static constexpr int TILE = kBN * LDP;           // elements per K or V tile
-  static constexpr int PAIRS = kBN * (D / 16);     // 16-byte chunk pairs (c, c + D/2) per tile
-  static constexpr int PPT = PAIRS / (64 * kNW);   // pairs per thread
-  static constexpr int NC = D / 16;                // 16-wide k-chunks of D
-  static constexpr int NDB = D / 32;               // 32-row blocks of D in O^T
-  static_assert(PAIRS % (64 * kNW) == 0, "tile split");
+  static constexpr int ROWB = D * 2;              // bytes per tile row (no padding)
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int TILEB = kBN * ROWB;        // bytes per K or V tile
+  static constexpr int NI = kBN * CPR / (64 * kNW);  // direct loads per wave per tile
+  static constexpr int NC = D / 16;               // 16-wide k-chunks of D
+  static constexpr int NDB = D / 32;              // 32-row blocks of D in O^T
+  static constexpr int PAIRS = kBN * (D / 16);    // rotary staging: chunk pairs (c, c + D/2) per tile
+  static constexpr int PPT = PAIRS / (64 * kNW);
+  __device__ static __forceinline__ int mask(int r) { return swz_mask<D>(r); }
 };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
@@ -54,10 +61,11 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p;
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2][2][C::TILE];  // [buf][K,V]
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][C::TILEB];  // [buf][K,V]
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, h = l >> 5, lq = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, h = l >> 5, lq = l & 31;
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = L / n_qt;
@@ -97,49 +105,80 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     }
   }
 
+  // Make the Q loads complete here, before the key loop: otherwise the compiler
+  // waits for them inside the loop, where the wait would also cover the next
+  // tile's in-flight LDS loads.
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]));
+
   // ---- key range of this workgroup
   const int last_row = (q0 + kBM < a.row_end ? q0 + kBM : a.row_end) - 1;
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
   const int n_kt = (n_vis + kBN - 1) / kBN;
+  // Positions increase with the local index, so the keys a query sees are the prefix
+  // [0, lim) of the block; the wave's first row has the smallest limit.
   const int wave_first = q0 + 32 * w < a.row_end ? q0 + 32 * w : a.row_end - 1;
-  const int wave_min_pos = a.qm.pos(wave_first);
+  const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
+  const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
 
-  // ---- global -> register staging of one K/V tile (chunk pairs c, c + D/2 of a row)
-  u32x4 kr[2 * C::PPT], vr[2 * C::PPT];
-  f32x4 tr[ROPE ? 4 * C::PPT : 1];  // rotary (cos, sin) pairs for the K chunk pairs
-  auto load_tile = [&](int kt) {
+  // ---- direct global -> LDS loads: wave w fills 1 KB slots w*NI .. w*NI+NI-1 of each tile.
+  // Slot position p = 64*slot + lane is tile row p / CPR, physical chunk p % CPR. The lane's
+  // byte offsets from the tile's first key row are fixed; only the (scalar) tile base moves.
+  int ld_row[C::NI], ld_col[C::NI];
+  unsigned ko[C::NI], vo[C::NI];
 #pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int p = tid + 64 * kNW * i;
-      const int r = p / (D / 16), cp = p % (D / 16);
-      const int key = kt * kBN + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kr[2 * i] = kr[2 * i + 1] = vr[2 * i] = vr[2 * i + 1] = z;
-      if (key < a.Tk) {
+  for (int i = 0; i < C::NI; ++i) {
+    const int p = (w * C::NI + i) * 64 + l;
+    const int r = p / C::CPR;
+    ld_row[i] = r;
+    ld_col[i] = ((p % C::CPR) ^ C::mask(r)) * 8;
+    ko[i] = (unsigned)((r * a.k.st + ld_col[i]) * 2);
+    vo[i] = (unsigned)((r * a.v.st + ld_col[i]) * 2);
+  }
+  auto issue_tile = [&](int kt, int buf) {
+    const char* kbase = (const char*)(kp + (int64_t)kt * kBN * a.k.st);
+    const char* vbase = (const char*)(vp + (int64_t)kt * kBN * a.v.st);
+    const bool tail = kt * kBN + kBN > a.Tk;  // rows past the block repeat the last key (masked later)
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      unsigned k_off = ko[i], v_off = vo[i];
+      if (tail) {
+        const int r = min(ld_row[i], a.Tk - 1 - kt * kBN);
+        k_off = (unsigned)((r * a.k.st + ld_col[i]) * 2);
+        v_off = (unsigned)((r * a.v.st + ld_col[i]) * 2);
+      }
+      if constexpr (!ROPE) load_lds16(kbase, k_off, smem[buf][0] + (w * C::NI + i) * 1024);
+      load_lds16(vbase, v_off, smem[buf][1] + (w * C::NI + i) * 1024);
+    }
+  };
+  // rotary: K chunk pairs (c, c + D/2) of a row through registers
+  u32x4 kr[ROPE ? 2 * C::PPT : 1];
+  f32x4 tr[ROPE ? 4 * C::PPT : 1];
+  auto load_k_regs = [&](int kt) {
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int i = 0; i < C::PPT; ++i) {
+        const int p = tid + 64 * kNW * i;
+        const int r = p / (D / 16), cp = p % (D / 16);
+        int key = kt * kBN + r;
+        key = key < a.Tk ? key : a.Tk - 1;
         const __bf16* kk = kp + (int64_t)key * a.k.st + 8 * cp;
-        const __bf16* vv = vp + (int64_t)key * a.v.st + 8 * cp;
         kr[2 * i] = ldg16(kk);
         kr[2 * i + 1] = ldg16(kk + D / 2);
-        vr[2 * i] = ldg16(vv);
-        vr[2 * i + 1] = ldg16(vv + D / 2);
-        if constexpr (ROPE) {
-          const f32x4* tb = (const f32x4*)(a.rope + (int64_t)a.km.pos(key) * D + 16 * cp);
+        const f32x4* tb = (const f32x4*)(a.rope + (int64_t)a.km.pos(key) * D + 16 * cp);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) tr[4 * i + j] = tb[j];
-        }
+        for (int j = 0; j < 4; ++j) tr[4 * i + j] = tb[j];
       }
     }
   };
-  auto store_tile = [&](int buf) {
-    __bf16* ks = smem[buf][0];
-    __bf16* vs = smem[buf][1];
+  auto store_k_regs = [&](int buf) {
+    if constexpr (ROPE) {
+      char* ks = smem[buf][0];
 #pragma unroll
-    for (int i = 0; i < C::PPT; ++i) {
-      const int p = tid + 64 * kNW * i;
-      const int r = p / (D / 16), cp = p % (D / 16);
-      u32x4 k0 = kr[2 * i], k1 = kr[2 * i + 1];
-      if constexpr (ROPE) {
-        bf16x8 x1 = __builtin_bit_cast(bf16x8, k0), x2 = __builtin_bit_cast(bf16x8, k1);
+      for (int i = 0; i < C::PPT; ++i) {
+        const int p = tid + 64 * kNW * i;
+        const int r = p / (D / 16), cp = p % (D / 16);
+        const bf16x8 x1 = __builtin_bit_cast(bf16x8, kr[2 * i]), x2 = __builtin_bit_cast(bf16x8, kr[2 * i + 1]);
         bf16x8 y1, y2;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -148,15 +187,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
           y1[e] = (__bf16)(f1 * cs - f2 * sn);
           y2[e] = (__bf16)(f2 * cs + f1 * sn);
         }
-        k0 = __builtin_bit_cast(u32x4, y1);
-        k1 = __builtin_bit_cast(u32x4, y2);
+        const int m = C::mask(r);
+        *(bf16x8*)(ks + r * C::ROWB + ((cp ^ m) * 16)) = y1;
+        *(bf16x8*)(ks + r * C::ROWB + (((cp + C::CPR / 2) ^ m) * 16)) = y2;
       }
-      *(u32x4*)(ks + r * C::LDP + 8 * cp) = k0;
-      *(u32x4*)(ks + r * C::LDP + 8 * cp + D / 2) = k1;
-      *(u32x4*)(vs + r * C::LDP + 8 * cp) = vr[2 * i];
-      *(u32x4*)(vs + r * C::LDP + 8 * cp + D / 2) = vr[2 * i + 1];
     }
   };
+
+  // ---- per-lane LDS byte offsets (swizzled)
+  // K operand: row 32kb + lq, logical chunk 2c + h
+  int koff[C::NC];
+  {
+    const int m = C::mask(lq);
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) koff[c] = lq * C::ROWB + (((2 * c + h) ^ m) * 16);
+  }
+  // V^T operand (transposing read): rows 16t + 4h + (l%16)/4 (+8), column 32db + 16((l/16)%2) + 4(l%4)
+  int voff[2][C::NDB];
+  {
+    const int r0 = 4 * h + ((l & 15) >> 2);
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = r0 + 8 * hi;
+      const int m = C::mask(r);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const int cc = 4 * db + 2 * ((l >> 4) & 1) + ((l & 3) >> 1);
+        voff[hi][db] = r * C::ROWB + ((cc ^ m) * 16) + (l & 1) * 8;
+      }
+    }
+  }
 
   f32x16 acc[C::NDB];
 #pragma unroll
@@ -165,47 +225,50 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   const float sl2 = a.scale * kLog2e;
 
   if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
+    issue_tile(0, 0);
+    load_k_regs(0);
+    store_k_regs(0);
   }
-  __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
-    const __bf16* ks = smem[cur][0];
-    const __bf16* vs = smem[cur][1];
+    wait_vm0();
+    __syncthreads();  // tile kt in LDS for every wave; every wave is done with tile kt-1's buffer
+    if (kt + 1 < n_kt) {
+      issue_tile(kt + 1, cur ^ 1);
+      load_k_regs(kt + 1);
+    }
+    const char* ks = smem[cur][0];
+    const char* vs = smem[cur][1];
 
     // ---- S^T = K Q^T for two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const __bf16* kr0 = ks + (32 * kb + lq) * C::LDP + 8 * h;
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) s[kb] = mfma32(*(const bf16x8*)(kr0 + 16 * c), qf[c], s[kb]);
+      for (int c = 0; c < C::NC; ++c)
+        s[kb] = mfma32(*(const bf16x8*)(ks + 32 * kb * C::ROWB + koff[c]), qf[c], s[kb]);
     }
 
-    // ---- mask (tiles that straddle the diagonal or the end of the block)
+    // ---- mask: keys at or past this row's limit (only tiles that reach past the wave's smallest limit)
     const int k0 = kt * kBN;
-    const bool full = (k0 + kBN <= a.Tk) && (!a.causal || a.km.pos(k0 + kBN - 1) <= wave_min_pos);
-    if (!full) {
+    if (k0 + kBN > wave_lim) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool vis = key < a.Tk && (!a.causal || a.km.pos(key) <= qpos);
-          if (!vis) s[kb][r] = -INFINITY;
+          s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
         }
     }
 
     // ---- row max (lane + lane^32), lazy rescale
-    float mx = s[0][0];
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_tile = mx * sl2;
     const bool need = m_tile > m_run + kRescaleSlack;
@@ -221,32 +284,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     }
     const float mu = m_run == -INFINITY ? 0.f : m_run;
 
-    // ---- P = exp2(S * sigma * log2e - m), row sum, bf16 pack
+    // ---- P = exp2(S * sigma * log2e - m), bf16 pack
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[kb][r], sl2, -mu));
-        l_part += p;
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)p;
+        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(fmaf(s[kb][r], sl2, -mu));
       }
+    // row sum of the bf16 weights the PV product uses
+#pragma unroll
+    for (int t = 0; t < 4; ++t) l_part = sum8_bf16(pb[t], l_part);
 
     // ---- O^T += V^T P^T ; V^T operand rows = d, 8 keys: 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
-        const int col = 32 * db + 16 * ((l >> 4) & 1) + 4 * (l & 3);
-        const int rr = 16 * t + 4 * h + ((l & 15) >> 2);
-        const bf16x4 lo = lds_read_tr4(vs + rr * C::LDP + col);
-        const bf16x4 hi = lds_read_tr4(vs + (rr + 8) * C::LDP + col);
+        const char* base = vs + 16 * t * C::ROWB;
+        const bf16x4 lo = lds_read_tr4((const __bf16*)(base + voff[0][db]));
+        const bf16x4 hi = lds_read_tr4((const __bf16*)(base + voff[1][db]));
         acc[db] = mfma32(cat8(lo, hi), pb[t], acc[db]);
       }
     }
 
-    if (kt + 1 < n_kt) store_tile(cur ^ 1);
-    __syncthreads();
+    if (kt + 1 < n_kt) store_k_regs(cur ^ 1);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
