@@ -21,8 +21,10 @@ BUILD = os.path.join(ROOT, "_build", "libcpattn")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are disabled for all device code. MFMA accumulators
+# are kept in VGPRs: otherwise the compiler parks loop-carried accumulators in
+# AGPRs and copies them back and forth every iteration.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Wall", "-Wno-unused-result"]
 

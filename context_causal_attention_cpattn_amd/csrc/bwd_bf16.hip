@@ -71,13 +71,13 @@ struct Offs {
 // ------------------------------------------------------------------ dK / dV
 constexpr int kKeysPerWG = 32 * kNW;  // 128
 
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   using C = BCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char sq[2][C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sdo[2][C::TILEB];
-  __shared__ __attribute__((aligned(16))) float slse[2][kTile];
-  __shared__ __attribute__((aligned(16))) float sdelta[2][kTile];
+  __shared__ __attribute__((aligned(1024))) char sq[NS][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sdo[NS][C::TILEB];
+  __shared__ __attribute__((aligned(16))) float slse[NS][kTile];
+  __shared__ __attribute__((aligned(16))) float sdelta[NS][kTile];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -133,7 +133,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
     qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
     oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
   }
-  float rl = 0.f, rd = 0.f;
+  // LSE and delta rows of a tile: every wave brings 16 of the 64 (lanes 0..15)
+  const unsigned lo_lse = (unsigned)((16 * w + (l & 15)) * a.lse.st * 4);
+  const unsigned lo_dl = (unsigned)((16 * w + (l & 15)) * a.delta.st * 4);
   auto issue_tile = [&](int t, int buf) {
     const int q0 = t * kTile;
     const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
@@ -150,21 +152,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
       load_lds16(qbase, q_off, sq[buf] + (w * C::NI + i) * 1024);
       load_lds16(obase, o_off, sdo[buf] + (w * C::NI + i) * 1024);
     }
-    if (tid < kTile) {
-      const int qrow = q0 + tid;
-      rl = INFINITY;  // rows past the end (or without any visible key) give P = 0
-      rd = 0.f;
-      if (qrow < a.Tq) {
-        const float L = lp[(int64_t)qrow * a.lse.st];
-        rl = L == -INFINITY ? INFINITY : L * kLog2e;
-        rd = dp[(int64_t)qrow * a.delta.st];
+    if (l < 16) {
+      unsigned l_off = lo_lse, d_off = lo_dl;
+      if (tail) {
+        const int r = min(16 * w + l, a.Tq - 1 - q0);
+        l_off = (unsigned)(r * a.lse.st * 4);
+        d_off = (unsigned)(r * a.delta.st * 4);
       }
-    }
-  };
-  auto store_rows = [&](int buf) {
-    if (tid < kTile) {
-      slse[buf][tid] = rl;
-      sdelta[buf][tid] = rd;
+      load_lds4(lp + (int64_t)q0 * a.lse.st, l_off, &slse[buf][16 * w]);
+      load_lds4(dp + (int64_t)q0 * a.delta.st, d_off, &sdelta[buf][16 * w]);
     }
   };
 
@@ -173,16 +169,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-  if (t_begin < t_end) {
-    issue_tile(t_begin, 0);
-    store_rows(0);
-  }
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (t_begin + j < t_end) issue_tile(t_begin + j, j);
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) & 1;
-    wait_vm0();
+    const int cur = (t - t_begin) % NS;
+    wait_tiles<2 * C::NI + 2>(min(NS - 2, t_end - 1 - t));
     __syncthreads();
-    if (t + 1 < t_end) issue_tile(t + 1, cur ^ 1);
+    if (t + NS - 1 < t_end) issue_tile(t + NS - 1, (t - t_begin + NS - 1) % NS);
     const char* Q = sq[cur];
     const char* DO = sdo[cur];
     const int q0 = t * kTile;
@@ -199,12 +194,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
       bf16x8 pa[2], dsa[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        // raw LSE: -L log2e; a row without any visible key (LSE = -inf) only occurs in
+        // tiles that are not full, where the mask below replaces its weights by 0
         const f32x4 L4 = *(const f32x4*)(slse[cur] + 32 * qb + 8 * g + 4 * h);
         const f32x4 D4 = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = 4 * g + j;
-          float p = fast_exp2(fmaf(s[r], sl2, -L4[j]));
+          float p = fast_exp2(fmaf(s[r], sl2, L4[j] * -kLog2e));
           if (!full) {
             const int qrow = q0 + 32 * qb + 8 * g + 4 * h + j;
             p = (key_ok && qrow >= qlo && qrow < a.Tq) ? p : 0.f;
@@ -229,7 +226,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
         }
       }
     }
-    if (t + 1 < t_end) store_rows(cur ^ 1);
   }
 
   if (t_begin >= t_end) return;  // no query of this block sees these keys: nothing to add
@@ -253,11 +249,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
 // ------------------------------------------------------------------ dQ
 constexpr int kQPerWG = 32 * kNW;  // 128
 
-template <int D>
+template <int D, int NS>
 __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
   using C = BCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char sk[2][C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sv[2][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sk[NS][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char sv[NS][C::TILEB];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -337,13 +333,15 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
-  if (n_kt > 0) issue_tile(0, 0);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) issue_tile(j, j);
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt & 1;
-    wait_vm0();
+    const int cur = kt % NS;
+    wait_tiles<2 * C::NI>(min(NS - 2, n_kt - 1 - kt));
     __syncthreads();
-    if (kt + 1 < n_kt) issue_tile(kt + 1, cur ^ 1);
+    if (kt + NS - 1 < n_kt) issue_tile(kt + NS - 1, (kt + NS - 1) % NS);
     const char* K = sk[cur];
     const char* V = sv[cur];
     const int k0 = kt * kTile;
@@ -395,18 +393,23 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
   }
 }
 
+#ifndef CPATTN_BWD_NS128
+#define CPATTN_BWD_NS128 2
+#endif
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
+  constexpr int NS = D == 64 ? 4 : CPATTN_BWD_NS128;
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;
   if (which & 1) {
-    hipLaunchKernelGGL((dkdv_kernel<D>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    hipLaunchKernelGGL((dkdv_kernel<D, NS>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
-    hipLaunchKernelGGL((dq_kernel<D>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
+    hipLaunchKernelGGL((dq_kernel<D, NS>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -99,6 +99,29 @@ __device__ __forceinline__ float sum8_bf16(const bf16x8& v, float acc) {
 
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 4 bytes per lane into LDS at lds_wave_base + 4 * lane (global_load_lds_dword).
+__device__ __forceinline__ void load_lds4(const void* base, unsigned off, const void* lds_wave_base) {
+  const unsigned lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
+// Wait until at most `later * PER` of this wave's vector loads are outstanding,
+// i.e. until every tile issued before the `later` most recent ones has landed
+// (loads complete in issue order). `later` is wave-uniform and < 4.
+template <int PER>
+__device__ __forceinline__ void wait_tiles(int later) {
+  if (later <= 0) wait_vm<0>();
+  else if (later == 1) wait_vm<PER>();
+  else if (later == 2) wait_vm<2 * PER>();
+  else wait_vm<3 * PER>();
+}
+
 // Workgroup id -> logical tile id so that consecutive logical tiles land on
 // the same XCD. Workgroups are dealt to the 8 XCDs round-robin by id, so XCD x
 // runs ids x, x+8, x+16, ...; logical tiles [x*per + min(x,rem), ...) go there.

@@ -58,10 +58,14 @@ struct Cfg {
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
-template <int D, bool ROPE>
+// NS: LDS pipeline depth (tiles in flight + the one being read). The rotary
+// variant stages K through registers, so it keeps two stages.
+template <int D, bool ROPE, int NS>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][C::TILEB];  // [buf][K,V]
+  static_assert(!ROPE || NS == 2, "rotary variant is double buffered");
+  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) char smem[NS][2][C::TILEB];  // [stage][K,V]
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -224,18 +228,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = a.scale * kLog2e;
 
+  // prologue: tiles 0 .. NS-2 in flight
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) issue_tile(j, j);
   if (n_kt > 0) {
-    issue_tile(0, 0);
     load_k_regs(0);
     store_k_regs(0);
   }
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt & 1;
-    wait_vm0();
-    __syncthreads();  // tile kt in LDS for every wave; every wave is done with tile kt-1's buffer
-    if (kt + 1 < n_kt) {
-      issue_tile(kt + 1, cur ^ 1);
+    const int cur = kt % NS;
+    // tile kt has landed for this wave once only the tiles issued after it are outstanding
+    const int later = min(NS - 2, n_kt - 1 - kt);
+    if constexpr (ROPE) wait_vm0();
+    else wait_tiles<(ROPE ? 1 : 2) * C::NI>(later);
+    __syncthreads();  // tile kt visible to every wave; every wave is done with tile kt-1's stage
+    if (kt + NS - 1 < n_kt) {
+      issue_tile(kt + NS - 1, (kt + NS - 1) % NS);
       load_k_regs(kt + 1);
     }
     const char* ks = smem[cur][0];
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
       }
     }
 
-    if (kt + 1 < n_kt) store_k_regs(cur ^ 1);
+    if (kt + 1 < n_kt) store_k_regs((kt + 1) % NS);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
@@ -333,13 +343,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   }
 }
 
+#ifndef CPATTN_FWD_NS128
+#define CPATTN_FWD_NS128 2
+#endif
+
 template <int D, bool ROPE>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
   const int n_qt = (rows + kBM - 1) / kBM;
   const int64_t grid = (int64_t)n_qt * a.B * a.H;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROPE>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
+  constexpr int NS = ROPE ? 2 : (D == 64 ? 4 : CPATTN_FWD_NS128);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROPE, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
