@@ -184,51 +184,73 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
     const bool full = (q0 + kTile <= a.Tq) && (kw0 + 31 < a.Tk) && (q0 >= wave_qlo);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      // operands of S = Q K^T and dP = dO V^T for 32 query rows, read as one batch
+      bf16x8 qa[C::NC], da[C::NC];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        qa[c] = *(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]);
+        da[c] = *(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{}, dpv = f32x16{};
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        s = mfma32(*(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]), kf[c], s);
-        dpv = mfma32(*(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]), vf[c], dpv);
+        s = mfma32(qa[c], kf[c], s);
+        dpv = mfma32(da[c], vf[c], dpv);
       }
       // rows of s / dpv: query 32qb + 8g + 4h + j, column: this lane's key
-      bf16x8 pa[2], dsa[2];
+      f32x4 L4[4], D4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        // raw LSE: -L log2e; a row without any visible key (LSE = -inf) only occurs in
-        // tiles that are not full, where the mask below replaces its weights by 0
-        const f32x4 L4 = *(const f32x4*)(slse[cur] + 32 * qb + 8 * g + 4 * h);
-        const f32x4 D4 = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
+        L4[g] = *(const f32x4*)(slse[cur] + 32 * qb + 8 * g + 4 * h);
+        D4[g] = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
+      }
+      // raw LSE: -L log2e; a row without any visible key (LSE = -inf) only occurs in
+      // tiles that are not full, where the mask below replaces its weights by 0
+      float p[16];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          float p = fast_exp2(fmaf(s[r], sl2, L4[j] * -kLog2e));
-          if (!full) {
-            const int qrow = q0 + 32 * qb + 8 * g + 4 * h + j;
-            p = (key_ok && qrow >= qlo && qrow < a.Tq) ? p : 0.f;
-          }
-          const float ds = p * (dpv[r] - D4[j]);
-          pa[r >> 3][r & 7] = (__bf16)p;
-          dsa[r >> 3][r & 7] = (__bf16)ds;
+      for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], sl2, L4[r >> 2][r & 3] * -kLog2e));
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+          p[r] = (key_ok && qrow >= qlo && qrow < a.Tq) ? p[r] : 0.f;
         }
+      }
+      bf16x8 pa[2], dsa[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pa[r >> 3][r & 7] = (__bf16)p[r];
+        dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
       }
       // dV += P^T dO, dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int rb = (32 * qb + 16 * tt) * C::ROWB;
+        bf16x8 ob[C::NDB], qv[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          const bf16x8 ob = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
-                                 lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
-          dv[db] = mfma32(pa[tt], ob, dv[db]);
-          const bf16x8 qv = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
-                                 lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
-          dk[db] = mfma32(dsa[tt], qv, dk[db]);
+          ob[db] = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
+                        lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
+          qv[db] = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
+                        lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          mfma32_agpr(dv[db], pa[tt], ob[db]);
+          mfma32_agpr(dk[db], dsa[tt], qv[db]);
         }
       }
     }
   }
 
   if (t_begin >= t_end) return;  // no query of this block sees these keys: nothing to add
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    mfma_agpr_drain(dk[db]);
+    mfma_agpr_drain(dv[db]);
+  }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j
   float* dkp = a.dk + b * a.dk_sb + hh * a.dk_sh;
   float* dvp = a.dv + b * a.dv_sb + hh * a.dv_sh;
@@ -370,11 +392,10 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
     for (int t = 0; t < 4; ++t) {
       const int rb = 16 * t * C::ROWB;
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const bf16x8 kt8 = cat8(lds_read_tr4((const __bf16*)(K + rb + off.tro[0][db])),
-                                lds_read_tr4((const __bf16*)(K + rb + off.tro[1][db])));
-        acc[db] = mfma32(kt8, dsb[t], acc[db]);
-      }
+      for (int db = 0; db < C::NDB; ++db)
+        acc[db] = mfma32(cat8(lds_read_tr4((const __bf16*)(K + rb + off.tro[0][db])),
+                              lds_read_tr4((const __bf16*)(K + rb + off.tro[1][db]))),
+                         dsb[t], acc[db]);
     }
   }
 

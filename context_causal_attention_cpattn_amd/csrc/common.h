@@ -39,6 +39,23 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same product with the accumulator held in AGPRs (the "a" constraint).
+// Used for long-lived accumulators so that they do not compete with the
+// working set for VGPRs. The compiler cannot see into the asm, so the wait
+// states it would otherwise insert are written here: two before the MFMA (a
+// VALU write of an operand VGPR followed by the MFMA read); a dependent MFMA on
+// the same accumulator needs none. Before the accumulator is read by anything
+// else, call mfma_agpr_drain on it.
+__device__ __forceinline__ void mfma32_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// 24 wait states after the last MFMA writing `acc` (a 16-pass 32x32 MFMA result
+// is read back by a VALU/accvgpr instruction); chained through `acc` so that the
+// compiler cannot move the read above it.
+__device__ __forceinline__ void mfma_agpr_drain(f32x16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc));
+}
+
 // Transposing LDS read of a 4-row x 16-column block of 16-bit values.
 // Within every group of 16 lanes, output lane i element e is element (i % 4)
 // of the 8 bytes addressed by source lane 4*e + i/4. To give lane i the

@@ -251,14 +251,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     const char* ks = smem[cur][0];
     const char* vs = smem[cur][1];
 
-    // ---- S^T = K Q^T for two 32-key blocks
+    // ---- S^T = K Q^T for two 32-key blocks (operands read as one batch per block)
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[C::NC];
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) ka[c] = *(const bf16x8*)(ks + 32 * kb * C::ROWB + koff[c]);
+      __builtin_amdgcn_sched_barrier(0);
       s[kb] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c)
-        s[kb] = mfma32(*(const bf16x8*)(ks + 32 * kb * C::ROWB + koff[c]), qf[c], s[kb]);
+      for (int c = 0; c < C::NC; ++c) s[kb] = mfma32(ka[c], qf[c], s[kb]);
     }
 
     // ---- mask: keys at or past this row's limit (only tiles that reach past the wave's smallest limit)
@@ -309,13 +312,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     // ---- O^T += V^T P^T ; V^T operand rows = d, 8 keys: 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const char* base = vs + 16 * t * C::ROWB;
+      bf16x8 va[C::NDB];
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const char* base = vs + 16 * t * C::ROWB;
-        const bf16x4 lo = lds_read_tr4((const __bf16*)(base + voff[0][db]));
-        const bf16x4 hi = lds_read_tr4((const __bf16*)(base + voff[1][db]));
-        acc[db] = mfma32(cat8(lo, hi), pb[t], acc[db]);
-      }
+      for (int db = 0; db < C::NDB; ++db)
+        va[db] = cat8(lds_read_tr4((const __bf16*)(base + voff[0][db])),
+                      lds_read_tr4((const __bf16*)(base + voff[1][db])));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(va[db], pb[t], acc[db]);
     }
 
     if (kt + 1 < n_kt) store_k_regs((kt + 1) % NS);
