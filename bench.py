@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
     ap.add_argument("--no-graph", action="store_true", help="time eager steps instead of graph replays")
+    ap.add_argument("--split-bwd", action="store_true",
+                    help="call the two halves of the block backward separately (per-half timings)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch of the dominant kernel (from rocprofv3 --pmc)")
     return ap.parse_args()
@@ -99,9 +101,14 @@ class Share:
         self.pairs = sum(p for _, _, p in self.steps)
         self.bh = w.B * w.H
 
+    split_bwd = False
+
     def build_plan(self, do_bwd=True):
         """Marshal every launch of one step once: (name, work, fn, args). The calls are the
-        library's C entry points with the same arguments the binding would pass."""
+        library's C entry points with the same arguments the binding would pass. The block
+        backward is one cpattn_block_bwd call per ring step (one grid for both halves at
+        D = 64, two launches at D = 128); ``split_bwd`` times its two halves separately."""
+        split_bwd = self.split_bwd
         cp, w = self.cp, self.w
         lib = cp.load()
         T = cp._tensor
@@ -137,6 +144,11 @@ class Share:
                 k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
                 dk, dv = T(self.dk[src]), T(self.dv[src])
                 keep += [k, v, km, dk, dv]
+                if not split_bwd:
+                    plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd,
+                                 (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
+                                  B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, st)))
+                    continue
                 plan.append(("block_bwd_dkdv", 8 * D * pairs * self.bh, lib.cpattn_block_bwd_dkdv,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dk), by(dv), B, H, Tl, Tk, D,
                               by(qm), by(km), 1, 0.0, st)))
@@ -184,8 +196,8 @@ class _no_event:
 class EventLog:
     """HIP events around each launch on torch's current stream (the library's stream)."""
 
-    BOUND = {"block_fwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma", "lse_merge": "hbm",
-             "bwd_preprocess": "hbm"}
+    BOUND = {"block_fwd": "mfma", "block_bwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma",
+             "lse_merge": "hbm", "bwd_preprocess": "hbm"}
 
     def __init__(self):
         self.rec = []
@@ -350,6 +362,7 @@ def main():
     from workloads import BY_NAME
     w = BY_NAME[args.workload]
     share = Share(w, seed_do=w.seed + 1000)
+    share.split_bwd = args.split_bwd
     wall, kern, graphed = time_steps(share, args.steps, args.warmup, graph=not args.no_graph)
     flops = share.flops()
     value = flops / wall / 1e12
@@ -393,6 +406,7 @@ def main():
         for name in ("win16k", "win32k"):
             wx = BY_NAME[name]
             sx = Share(wx, seed_do=wx.seed + 1000)
+            sx.split_bwd = True  # at D = 128 the two halves are separate launches anyway
             bwd = name == "win16k"
             wl, kx, _ = time_steps(sx, 3, 1, do_bwd=bwd)
             fl = sx.flops(bwd)

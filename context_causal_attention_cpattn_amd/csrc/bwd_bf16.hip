@@ -72,17 +72,25 @@ struct Offs {
 constexpr int kKeysPerWG = 32 * kNW;  // 128
 
 template <int D, int NS>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
+struct DkdvLds {
+  alignas(1024) char sq[NS][BCfg<D>::TILEB];
+  alignas(1024) char sdo[NS][BCfg<D>::TILEB];
+  alignas(16) float slse[NS][kTile];
+  alignas(16) float sdelta[NS][kTile];
+};
+
+// Workgroup Lg of the dK/dV grid (Lg = bh * n_kt + key tile).
+template <int D, int NS>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, DkdvLds<D, NS>& sm) {
   using C = BCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char sq[NS][C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sdo[NS][C::TILEB];
-  __shared__ __attribute__((aligned(16))) float slse[NS][kTile];
-  __shared__ __attribute__((aligned(16))) float sdelta[NS][kTile];
+  auto& sq = sm.sq;
+  auto& sdo = sm.sdo;
+  auto& slse = sm.slse;
+  auto& sdelta = sm.sdelta;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const int Lg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = Lg / n_kt;
   const int kt = Lg - bh * n_kt;
   const int b = bh / a.H, hh = bh - b * a.H;
@@ -272,15 +280,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
 constexpr int kQPerWG = 32 * kNW;  // 128
 
 template <int D, int NS>
-__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
+struct DqLds {
+  alignas(1024) char sk[NS][BCfg<D>::TILEB];
+  alignas(1024) char sv[NS][BCfg<D>::TILEB];
+};
+
+// Workgroup Lg of the dQ grid (Lg = bh * n_qt + heavy-first query tile).
+template <int D, int NS>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLds<D, NS>& sm) {
   using C = BCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char sk[NS][C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char sv[NS][C::TILEB];
+  auto& sk = sm.sk;
+  auto& sv = sm.sv;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const int Lg = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = Lg / n_qt;
   const int qt = n_qt - 1 - (Lg - bh * n_qt);
   const int b = bh / a.H, hh = bh - b * a.H;
@@ -414,6 +428,39 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
   }
 }
 
+template <int D, int NS>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
+  __shared__ DkdvLds<D, NS> sm;
+  dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
+  __shared__ DqLds<D, NS> sm;
+  dq_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
+}
+
+// Both halves of the block backward in one grid: the first n_dq workgroups (a
+// multiple of 8, the surplus idle) form dQ, the rest dK/dV. The two write
+// disjoint outputs, and sharing a grid lets them fill the chip together when
+// each alone is too small to. Workgroups are dealt to the 8 XCDs round-robin by
+// id, so both roles land on every XCD; within a role the ids are remapped as in
+// the single-role kernels.
+template <int D, int NS>
+__global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_dq, int n_dq_pad) {
+  __shared__ union {
+    DkdvLds<D, NS> kv;
+    DqLds<D, NS> q;
+  } sm;
+  const int id = blockIdx.x;
+  if (id < n_dq_pad) {
+    const int L = xcd_remap(id, n_dq_pad);
+    if (L < n_dq) dq_body<D, NS>(a, L, n_qt, sm.q);
+  } else {
+    dkdv_body<D, NS>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
+  }
+}
+
 #ifndef CPATTN_BWD_NS128
 #define CPATTN_BWD_NS128 2
 #endif
@@ -424,6 +471,16 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;
+  if constexpr (D == 64) {
+    // both kernels keep two workgroups per CU at this width, so one grid costs nothing
+    if (which == 3) {
+    const int64_t n_dq = bh * n_qt, n_dq_pad = (n_dq + 7) / 8 * 8;
+    const int64_t grid = n_dq_pad + bh * n_kt;
+    hipLaunchKernelGGL((bwd_fused_kernel<D, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt, n_qt,
+                       (int)n_dq, (int)n_dq_pad);
+    return hipGetLastError();
+    }
+  }
   if (which & 1) {
     hipLaunchKernelGGL((dkdv_kernel<D, NS>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();

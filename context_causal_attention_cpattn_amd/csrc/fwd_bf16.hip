@@ -28,10 +28,12 @@
 //     score exceeds it by more than 2^8, so the accumulator is rarely rescaled
 //     (exact: O and the row sum always share the same reference max);
 //   * workgroup ids are remapped so that the query tiles of one (b, h) run on
-//     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first.
-//   * with rotary embedding, K is staged through registers instead (it must be
-//     rotated at its global position before it reaches LDS); Q is rotated once
-//     in the prologue.
+//     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first;
+//   * the loop is software pipelined so that each wave keeps its matrix cores
+//     and its vector ALUs busy at the same time (see fwd_bf16_kernel).
+// The variant with fused rotary embedding lives in fwd_rope_bf16.hip.
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -51,21 +53,38 @@ struct Cfg {
   static constexpr int NI = kBN * CPR / (64 * kNW);  // direct loads per wave per tile
   static constexpr int NC = D / 16;               // 16-wide k-chunks of D
   static constexpr int NDB = D / 32;              // 32-row blocks of D in O^T
-  static constexpr int PAIRS = kBN * (D / 16);    // rotary staging: chunk pairs (c, c + D/2) per tile
-  static constexpr int PPT = PAIRS / (64 * kNW);
   __device__ static __forceinline__ int mask(int r) { return swz_mask<D>(r); }
 };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
-// NS: LDS pipeline depth (tiles in flight + the one being read). The rotary
-// variant stages K through registers, so it keeps two stages.
-template <int D, bool ROPE, int NS>
+// Wait until at most `units * PER` of this wave's vector loads are outstanding
+// (loads complete in issue order). `units` is wave-uniform, 0..4.
+template <int PER>
+__device__ __forceinline__ void wait_units(int units) {
+  switch (units) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<PER>(); break;
+    case 2: wait_vm<2 * PER>(); break;
+    case 3: wait_vm<3 * PER>(); break;
+    default: wait_vm<4 * PER>(); break;
+  }
+}
+
+// Software pipeline (per wave, per key tile j):
+//   top:     the scores S_j of tile j are already in registers, masked, with their row max;
+//            lazy rescale of the accumulator if the max moved
+//   phase A: P_j = exp2(S_j sigma log2e - m) (VALU)  interleaved with  S_{j+1} = K_{j+1} Q^T (MFMA)
+//   phase B: O^T += V_j^T P_j^T (MFMA)                 interleaved with  row max of S_{j+1} (VALU)
+// so that the matrix cores and the vector ALUs of one wave work at the same time.
+// LDS holds NS K tiles and NS V tiles. Load group g = {V_g, K_{g+1}} is issued
+// (in that order) at the top of iteration g - NS + 1 and consumed in iteration g.
+template <int D, int NS>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
-  static_assert(!ROPE || NS == 2, "rotary variant is double buffered");
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) char smem[NS][2][C::TILEB];  // [stage][K,V]
+  __shared__ __attribute__((aligned(1024))) char ksm[NS][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vsm[NS][C::TILEB];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -92,26 +111,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     qf[c] = __builtin_bit_cast(bf16x8, t);
   }
   const int qpos = a.qm.pos(row_ok ? row : a.row_end - 1);
-  if constexpr (ROPE) {
-    if (row_ok) {
-      const float* tb = a.rope + (int64_t)qpos * D;
-#pragma unroll
-      for (int c = 0; c < C::NC / 2; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 16 * c + 8 * h + e;
-          const float cs = tb[2 * i], sn = tb[2 * i + 1];
-          const float x1 = (float)qf[c][e], x2 = (float)qf[c + C::NC / 2][e];
-          qf[c][e] = (__bf16)(x1 * cs - x2 * sn);
-          qf[c + C::NC / 2][e] = (__bf16)(x2 * cs + x1 * sn);
-        }
-      }
-    }
-  }
-
   // Make the Q loads complete here, before the key loop: otherwise the compiler
-  // waits for them inside the loop, where the wait would also cover the next
-  // tile's in-flight LDS loads.
+  // waits for them inside the loop, where the wait would also cover the
+  // in-flight LDS loads of later tiles.
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]));
 
@@ -125,78 +127,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
 
-  // ---- direct global -> LDS loads: wave w fills 1 KB slots w*NI .. w*NI+NI-1 of each tile.
-  // Slot position p = 64*slot + lane is tile row p / CPR, physical chunk p % CPR. The lane's
-  // byte offsets from the tile's first key row are fixed; only the (scalar) tile base moves.
-  int ld_row[C::NI], ld_col[C::NI];
-  unsigned ko[C::NI], vo[C::NI];
+  // ---- direct global -> LDS loads: wave w fills the 1 KB slots w + kNW*i (i < NI) of each
+  // tile. Slot position p = 64*slot + lane is tile row p / CPR, physical chunk p % CPR. The
+  // rows of a lane's NI slots differ by 64*kNW/CPR, a multiple of the swizzle period, so the
+  // lane's byte offset is the same for all of them and only the (scalar) row base moves.
+  constexpr int kSlotRows = 64 * kNW / C::CPR;  // rows between a lane's consecutive slots
+  const int ld_r0 = (64 * w + l) / C::CPR;
+  const int ld_col = ((l % C::CPR) ^ C::mask(ld_r0)) * 8;
+  const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
+  const unsigned vo = (unsigned)((ld_r0 * a.v.st + ld_col) * 2);
+  // rows past the block repeat the last key (masked later)
+  static_assert(kSlotRows % 16 == 0, "slot rows must be a multiple of the swizzle period");
+  auto issue = [&](const __bf16* base, int64_t st, unsigned off, int kt, char* dst) {
+    const char* tb = (const char*)(base + (int64_t)kt * kBN * st);
+    if (kt * kBN + kBN <= a.Tk) {
 #pragma unroll
-  for (int i = 0; i < C::NI; ++i) {
-    const int p = (w * C::NI + i) * 64 + l;
-    const int r = p / C::CPR;
-    ld_row[i] = r;
-    ld_col[i] = ((p % C::CPR) ^ C::mask(r)) * 8;
-    ko[i] = (unsigned)((r * a.k.st + ld_col[i]) * 2);
-    vo[i] = (unsigned)((r * a.v.st + ld_col[i]) * 2);
-  }
-  auto issue_tile = [&](int kt, int buf) {
-    const char* kbase = (const char*)(kp + (int64_t)kt * kBN * a.k.st);
-    const char* vbase = (const char*)(vp + (int64_t)kt * kBN * a.v.st);
-    const bool tail = kt * kBN + kBN > a.Tk;  // rows past the block repeat the last key (masked later)
+      for (int i = 0; i < C::NI; ++i)
+        load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (w + kNW * i) * 1024);
+    } else {
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-      unsigned k_off = ko[i], v_off = vo[i];
-      if (tail) {
-        const int r = min(ld_row[i], a.Tk - 1 - kt * kBN);
-        k_off = (unsigned)((r * a.k.st + ld_col[i]) * 2);
-        v_off = (unsigned)((r * a.v.st + ld_col[i]) * 2);
-      }
-      if constexpr (!ROPE) load_lds16(kbase, k_off, smem[buf][0] + (w * C::NI + i) * 1024);
-      load_lds16(vbase, v_off, smem[buf][1] + (w * C::NI + i) * 1024);
-    }
-  };
-  // rotary: K chunk pairs (c, c + D/2) of a row through registers
-  u32x4 kr[ROPE ? 2 * C::PPT : 1];
-  f32x4 tr[ROPE ? 4 * C::PPT : 1];
-  auto load_k_regs = [&](int kt) {
-    if constexpr (ROPE) {
-#pragma unroll
-      for (int i = 0; i < C::PPT; ++i) {
-        const int p = tid + 64 * kNW * i;
-        const int r = p / (D / 16), cp = p % (D / 16);
-        int key = kt * kBN + r;
-        key = key < a.Tk ? key : a.Tk - 1;
-        const __bf16* kk = kp + (int64_t)key * a.k.st + 8 * cp;
-        kr[2 * i] = ldg16(kk);
-        kr[2 * i + 1] = ldg16(kk + D / 2);
-        const f32x4* tb = (const f32x4*)(a.rope + (int64_t)a.km.pos(key) * D + 16 * cp);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tr[4 * i + j] = tb[j];
+      for (int i = 0; i < C::NI; ++i) {
+        const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - kt * kBN);
+        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (w + kNW * i) * 1024);
       }
     }
   };
-  auto store_k_regs = [&](int buf) {
-    if constexpr (ROPE) {
-      char* ks = smem[buf][0];
-#pragma unroll
-      for (int i = 0; i < C::PPT; ++i) {
-        const int p = tid + 64 * kNW * i;
-        const int r = p / (D / 16), cp = p % (D / 16);
-        const bf16x8 x1 = __builtin_bit_cast(bf16x8, kr[2 * i]), x2 = __builtin_bit_cast(bf16x8, kr[2 * i + 1]);
-        bf16x8 y1, y2;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cs = tr[4 * i + e / 2][2 * (e % 2)], sn = tr[4 * i + e / 2][2 * (e % 2) + 1];
-          const float f1 = (float)x1[e], f2 = (float)x2[e];
-          y1[e] = (__bf16)(f1 * cs - f2 * sn);
-          y2[e] = (__bf16)(f2 * cs + f1 * sn);
-        }
-        const int m = C::mask(r);
-        *(bf16x8*)(ks + r * C::ROWB + ((cp ^ m) * 16)) = y1;
-        *(bf16x8*)(ks + r * C::ROWB + (((cp + C::CPR / 2) ^ m) * 16)) = y2;
-      }
-    }
+  auto issue_group = [&](int g) {
+    if (g < n_kt) issue(vp, a.v.st, vo, g, vsm[g % NS]);
+    if (g + 1 < n_kt) issue(kp, a.k.st, ko, g + 1, ksm[(g + 1) % NS]);
   };
+  auto group_units = [&](int g) { return (g < n_kt ? 1 : 0) + (g + 1 < n_kt ? 1 : 0); };
 
   // ---- per-lane LDS byte offsets (swizzled)
   // K operand: row 32kb + lq, logical chunk 2c + h
@@ -228,61 +188,71 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   float m_run = -INFINITY, l_part = 0.f;
   const float sl2 = a.scale * kLog2e;
 
-  // prologue: tiles 0 .. NS-2 in flight
+  // S^T block kb of the K tile in `ks` (operands read as one batch, then the MFMA chain)
+  auto scores = [&](const char* ks, int kb) {
+    bf16x8 ka[C::NC];
 #pragma unroll
-  for (int j = 0; j < NS - 1; ++j)
-    if (j < n_kt) issue_tile(j, j);
-  if (n_kt > 0) {
-    load_k_regs(0);
-    store_k_regs(0);
+    for (int c = 0; c < C::NC; ++c) ka[c] = *(const bf16x8*)(ks + 32 * kb * C::ROWB + koff[c]);
+    f32x16 r = f32x16{};
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) r = mfma32(ka[c], qf[c], r);
+    return r;
+  };
+  // Keys at or past this row's limit get -inf. Only tiles that reach past the
+  // wave's smallest limit can hold such keys.
+  auto needs_mask = [&](int kt) { return kt * kBN + kBN > wave_lim; };
+  // Element r of 32-key block kb is key kt*kBN + 32kb + 8(r/4) + 4h + r%4; with
+  // rel = lim - kt*kBN - 4h the test is a compare against a constant.
+  auto mask_rel = [&](int kt) { return lim - kt * kBN - 4 * h; };
+  auto mask_elem = [](float v, int rel, int kb, int r) {
+    return 32 * kb + 8 * (r >> 2) + (r & 3) < rel ? v : -INFINITY;
+  };
+
+  // ---- prologue: K_0, groups 0 .. NS-2, then S_0 and its row max
+  if (n_kt > 0) issue(kp, a.k.st, ko, 0, ksm[0]);
+  int pending = 0;  // load units issued after K_0
+#pragma unroll
+  for (int g = 0; g < NS - 1; ++g) {
+    issue_group(g);
+    pending += group_units(g);
   }
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt % NS;
-    // tile kt has landed for this wave once only the tiles issued after it are outstanding
-    const int later = min(NS - 2, n_kt - 1 - kt);
-    if constexpr (ROPE) wait_vm0();
-    else wait_tiles<(ROPE ? 1 : 2) * C::NI>(later);
-    __syncthreads();  // tile kt visible to every wave; every wave is done with tile kt-1's stage
-    if (kt + NS - 1 < n_kt) {
-      issue_tile(kt + NS - 1, (kt + NS - 1) % NS);
-      load_k_regs(kt + 1);
-    }
-    const char* ks = smem[cur][0];
-    const char* vs = smem[cur][1];
-
-    // ---- S^T = K Q^T for two 32-key blocks (operands read as one batch per block)
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 ka[C::NC];
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) ka[c] = *(const bf16x8*)(ks + 32 * kb * C::ROWB + koff[c]);
-      __builtin_amdgcn_sched_barrier(0);
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) s[kb] = mfma32(ka[c], qf[c], s[kb]);
-    }
-
-    // ---- mask: keys at or past this row's limit (only tiles that reach past the wave's smallest limit)
-    const int k0 = kt * kBN;
-    if (k0 + kBN > wave_lim) {
+  f32x16 sA[2] = {f32x16{}, f32x16{}}, sB[2];
+  float mx = -INFINITY;
+  if (n_kt > 0) {
+    wait_units<C::NI>(pending);
+    __syncthreads();
+    sA[0] = scores(ksm[0], 0);
+    sA[1] = scores(ksm[0], 1);
+    if (needs_mask(0)) {
+      const int rel = mask_rel(0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) sA[kb][r] = mask_elem(sA[kb][r], rel, kb, r);
     }
-
-    // ---- row max (lane + lane^32), lazy rescale
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float m = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sA[kb][r]);
+    mx = fmaxf(m, __shfl_xor(m, 32));
+  }
+
+  // One key tile. `sc` holds S_kt (masked) and `mx` its row max on entry; with
+  // NEXT, S_kt+1 is formed into `sn` (masked) and `mx` becomes its max.
+  // The interleaving is fixed by scheduling fences: each MFMA is followed by the
+  // slice of vector work that runs while it executes.
+  auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2], auto next_tag) __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    // group kt (V_kt, K_kt+1) has landed once only groups kt+1 .. kt+NS-2 are outstanding
+    int later = 0;
+#pragma unroll
+    for (int g = 1; g <= NS - 2; ++g) later += group_units(kt + g);
+    wait_units<C::NI>(later);
+    __syncthreads();  // group kt visible to all waves; all waves are done with V_kt-1 and K_kt
+    issue_group(kt + NS - 1);
+
+    // ---- lazy rescale: the running max moves only when a score exceeds it by 2^8
     const float m_tile = mx * sl2;
     const bool need = m_tile > m_run + kRescaleSlack;
     if (__any(need)) {
@@ -297,33 +267,104 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     }
     const float mu = m_run == -INFINITY ? 0.f : m_run;
 
-    // ---- P = exp2(S * sigma * log2e - m), bf16 pack
+    // ---- phase A: P_kt = exp2(S_kt sigma log2e - mu) in bf16 (+ row sum), while the
+    // matrix cores form S_kt+1 = K_kt+1 Q^T. The 2*NC K operands are read LA MFMAs ahead.
+    constexpr int EA = 16 / C::NC;  // score elements per MFMA slot
+    constexpr int LA = 4;
+    const char* kn = ksm[(kt + 1) % NS];
+    auto kread = [&](int j) { return *(const bf16x8*)(kn + 32 * (j / C::NC) * C::ROWB + koff[j % C::NC]); };
     bf16x8 pb[4];
+    bf16x8 ka[LA];
+    if constexpr (NEXT) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < LA; ++j) ka[j] = kread(j);
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(fmaf(s[kb][r], sl2, -mu));
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 acc_s = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        if constexpr (NEXT) {
+          const int j = C::NC * kb + c;
+          acc_s = mfma32(ka[j % LA], qf[c], acc_s);
+          if (j + LA < 2 * C::NC) ka[j % LA] = kread(j + LA);
+        }
+#pragma unroll
+        for (int e = 0; e < EA; ++e) {
+          const int r = EA * c + e;
+          pb[2 * kb + (r >> 3)][r & 7] = (__bf16)fast_exp2(fmaf(sc[kb][r], sl2, -mu));
+        }
+        if (EA * c + EA == 8) l_part = sum8_bf16(pb[2 * kb], l_part);
+        if (EA * c + EA == 16) l_part = sum8_bf16(pb[2 * kb + 1], l_part);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    // row sum of the bf16 weights the PV product uses
-#pragma unroll
-    for (int t = 0; t < 4; ++t) l_part = sum8_bf16(pb[t], l_part);
-
-    // ---- O^T += V^T P^T ; V^T operand rows = d, 8 keys: 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const char* base = vs + 16 * t * C::ROWB;
-      bf16x8 va[C::NDB];
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-        va[db] = cat8(lds_read_tr4((const __bf16*)(base + voff[0][db])),
-                      lds_read_tr4((const __bf16*)(base + voff[1][db])));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(va[db], pb[t], acc[db]);
+      if constexpr (NEXT) sn[kb] = acc_s;
     }
 
-    if (kt + 1 < n_kt) store_k_regs((kt + 1) % NS);
+    // ---- phase B: O^T += V^T P^T (V^T rows = d, 8 keys 16t + 4h + {0..3}, +8), while the
+    // vector ALUs take the row max of S_kt+1. V^T operands are read one MFMA ahead.
+    constexpr int EB = 32 / (4 * C::NDB);  // score elements per MFMA slot
+    const char* vs = vsm[kt % NS];
+    bf16x8 va[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+      va[db] = cat8(lds_read_tr4((const __bf16*)(vs + voff[0][db])),
+                    lds_read_tr4((const __bf16*)(vs + voff[1][db])));
+    float m2 = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        acc[db] = mfma32(va[db], pb[t], acc[db]);
+        if (t < 3) {
+          const char* base = vs + 16 * (t + 1) * C::ROWB;
+          va[db] = cat8(lds_read_tr4((const __bf16*)(base + voff[0][db])),
+                        lds_read_tr4((const __bf16*)(base + voff[1][db])));
+        }
+        if constexpr (NEXT) {
+#pragma unroll
+          for (int e = 0; e < EB; ++e) {
+            const int i = EB * (C::NDB * t + db) + e, kb = i >> 4, r = i & 15;
+            m2 = fmaxf(m2, sn[kb][r]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (NEXT) {
+      // a tile that reaches past the wave's smallest limit is masked and its max redone
+      asm volatile("" : "+v"(m2));  // keep the unmasked max beside the PV products
+      if (needs_mask(kt + 1)) {
+        const int rel = mask_rel(kt + 1);
+        m2 = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            sn[kb][r] = mask_elem(sn[kb][r], rel, kb, r);
+            m2 = fmaxf(m2, sn[kb][r]);
+          }
+      }
+      mx = fmaxf(m2, __shfl_xor(m2, 32));
+    }
+  };
+
+  using T_ = std::integral_constant<bool, true>;
+  using F_ = std::integral_constant<bool, false>;
+  auto run = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+    step(kt, sc, sn, T_{});
+  };
+  // two tiles per trip so that the score registers alternate instead of being copied
+  int kt = 0;
+  for (; kt + 2 < n_kt; kt += 2) {
+    run(kt, sA, sB);
+    run(kt + 1, sB, sA);
+  }
+  if (kt + 1 < n_kt) {
+    run(kt, sA, sB);
+    step(kt + 1, sB, sA, F_{});
+  } else if (kt < n_kt) {
+    step(kt, sA, sB, F_{});
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
@@ -348,27 +389,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   }
 }
 
-#ifndef CPATTN_FWD_NS128
-#define CPATTN_FWD_NS128 2
-#endif
-
-template <int D, bool ROPE>
+template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
   const int n_qt = (rows + kBM - 1) / kBM;
   const int64_t grid = (int64_t)n_qt * a.B * a.H;
   if (grid <= 0) return hipSuccess;
-  constexpr int NS = ROPE ? 2 : (D == 64 ? 4 : CPATTN_FWD_NS128);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, ROPE, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
+  constexpr int NS = D == 64 ? 4 : 2;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  const bool rope = a.rope != nullptr;
-  if (a.D == 64) return rope ? launch_d<64, true>(a, s) : launch_d<64, false>(a, s);
-  return rope ? launch_d<128, true>(a, s) : launch_d<128, false>(a, s);
+  if (a.rope != nullptr) return launch_fwd_rope_bf16(a, s);
+  return a.D == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
 }
 
 }  // namespace cpattn

@@ -66,6 +66,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_rope_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
 hipError_t launch_bwd_preprocess(const PreArgs& a, hipStream_t s);

@@ -204,8 +204,10 @@ int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn
  * dq_acc is [B,H,Tq,D] (the local rows), dk_acc and dv_acc are [B,H,Tk,D]
  * (the block's rows). The caller zeroes them once before the first step and
  * never between steps. bf16 inputs only; rotary is not supported here.
- * Two kernels (key-tile-major for dk/dv, query-tile-major for dq), no atomics:
- * results are bitwise reproducible.
+ * Two halves (key-tile-major for dk/dv, query-tile-major for dq), no atomics:
+ * results are bitwise reproducible and equal to calling the two halves below.
+ * At D = 64 both halves share one grid, so that a small block still fills the
+ * device; at D = 128 they are two launches.
  * Errors: as cpattn_block_fwd; EUNSUPPORTED for fp32 inputs.
  */
 int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
