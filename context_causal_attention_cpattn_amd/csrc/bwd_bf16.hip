@@ -20,6 +20,8 @@
 // Tiles are staged through LDS with direct global->LDS loads into the
 // swizzled, unpadded layout of common.h (double buffered, one barrier per tile).
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace cpattn {
@@ -277,20 +279,29 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 }
 
 // ------------------------------------------------------------------ dQ
-constexpr int kQPerWG = 32 * kNW;  // 128
+constexpr int kQPerWG = 32 * kNW;  // 128 query rows per workgroup
+constexpr int kKB = 32;            // keys per dQ tile: one 32-key MFMA block
 
 template <int D, int NS>
 struct DqLds {
-  alignas(1024) char sk[NS][BCfg<D>::TILEB];
-  alignas(1024) char sv[NS][BCfg<D>::TILEB];
+  alignas(1024) char sk[NS][kKB * BCfg<D>::ROWB];
+  alignas(1024) char sv[NS][kKB * BCfg<D>::ROWB];
 };
 
 // Workgroup Lg of the dQ grid (Lg = bh * n_qt + heavy-first query tile).
+// Software pipeline over the 32-key tiles u of the block (per wave):
+//   phase A: P_u, dS_u (VALU)  with  S_u+1^T = K Q^T (and at D = 64 dP_u+1^T = V dO^T) (MFMA)
+//   phase B: dQ^T += K_u^T dS_u^T (MFMA), K^T through the transposing LDS read
+//            (at D = 128 followed by dP_u+1^T, which keeps phase A within the registers of
+//            two waves per SIMD)
+// so tiles u and u+1 are read in iteration u, and the LDS ring holds NS >= 3 tiles.
 template <int D, int NS>
 __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLds<D, NS>& sm) {
   using C = BCfg<D>;
-  auto& sk = sm.sk;
-  auto& sv = sm.sv;
+  static_assert(NS >= 3 && NS <= 5, "pipeline depth");
+  constexpr int NIQ = kKB * C::CPR / (64 * kNW);  // direct loads per wave per tile (K or V)
+  constexpr int kSlotRows = 64 * kNW / C::CPR;    // rows between a lane's consecutive slots
+  static_assert(NIQ >= 1 && kSlotRows % 16 == 0, "tile layout");
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -302,9 +313,21 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   const int row = q0 + 32 * w + lq;
   const bool row_ok = row < a.Tq;
 
+  // ---- key range: the keys row r sees are the prefix [0, lim) of the block
+  const int qpos = a.qm.pos(row_ok ? row : a.Tq - 1);
+  const int last_row = (q0 + kQPerWG < a.Tq ? q0 + kQPerWG : a.Tq) - 1;
+  const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
+  const int n_kt = (n_vis + kKB - 1) / kKB;
+  if (n_kt == 0) return;  // no key of this block is visible to these rows: nothing to add
+  const int wave_first = q0 + 32 * w < a.Tq ? q0 + 32 * w : a.Tq - 1;
+  const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
+  const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
+  const float sl2 = a.scale * kLog2e;
+
   const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + hh * a.k.sh;
   const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + hh * a.v.sh;
 
+  // ---- Q and dO rows of this lane's query (B operands), LSE and delta of the row
   bf16x8 qf[C::NC], df[C::NC];
   {
     const __bf16* qq = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh + (int64_t)row * a.q.st;
@@ -327,41 +350,28 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]), "v"(df[c]));
   asm volatile("" ::"v"(lse2), "v"(dl));
 
-  const int qpos = a.qm.pos(row_ok ? row : a.Tq - 1);
-  const int last_row = (q0 + kQPerWG < a.Tq ? q0 + kQPerWG : a.Tq) - 1;
-  const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
-  const int n_kt = (n_vis + kTile - 1) / kTile;
-  // the keys this row sees are the prefix [0, lim) of the block (positions increase)
-  const int wave_first = q0 + 32 * w < a.Tq ? q0 + 32 * w : a.Tq - 1;
-  const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
-  const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
-  const float sl2 = a.scale * kLog2e;
-
-  int ld_row[C::NI], ld_col[C::NI];
-  unsigned ko[C::NI], vo[C::NI];
+  // ---- direct global -> LDS loads: wave w fills 1 KB slots w + kNW*i of each tile; the
+  // rows of a lane's slots differ by a multiple of the swizzle period (one lane offset)
+  const int ld_r0 = (64 * w + l) / C::CPR;
+  const int ld_col = ((l % C::CPR) ^ swz_mask<D>(ld_r0)) * 8;
+  const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
+  const unsigned vo = (unsigned)((ld_r0 * a.v.st + ld_col) * 2);
+  auto issue = [&](const __bf16* base, int64_t st, unsigned off, int kt, char* dst) {
+    const char* tb = (const char*)(base + (int64_t)kt * kKB * st);
+    if (kt * kKB + kKB <= a.Tk) {
 #pragma unroll
-  for (int i = 0; i < C::NI; ++i) {
-    const int p = (w * C::NI + i) * 64 + l;
-    ld_row[i] = p / C::CPR;
-    ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
-    ko[i] = (unsigned)((ld_row[i] * a.k.st + ld_col[i]) * 2);
-    vo[i] = (unsigned)((ld_row[i] * a.v.st + ld_col[i]) * 2);
-  }
-  auto issue_tile = [&](int kt, int buf) {
-    const char* kbase = (const char*)(kp + (int64_t)kt * kTile * a.k.st);
-    const char* vbase = (const char*)(vp + (int64_t)kt * kTile * a.v.st);
-    const bool tail = kt * kTile + kTile > a.Tk;  // rows past the block repeat the last key (masked)
+      for (int i = 0; i < NIQ; ++i) load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (w + kNW * i) * 1024);
+    } else {  // rows past the block repeat the last key (masked)
 #pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-      unsigned k_off = ko[i], v_off = vo[i];
-      if (tail) {
-        const int r = min(ld_row[i], a.Tk - 1 - kt * kTile);
-        k_off = (unsigned)((r * a.k.st + ld_col[i]) * 2);
-        v_off = (unsigned)((r * a.v.st + ld_col[i]) * 2);
+      for (int i = 0; i < NIQ; ++i) {
+        const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - kt * kKB);
+        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (w + kNW * i) * 1024);
       }
-      load_lds16(kbase, k_off, sk[buf] + (w * C::NI + i) * 1024);
-      load_lds16(vbase, v_off, sv[buf] + (w * C::NI + i) * 1024);
     }
+  };
+  auto issue_tile = [&](int kt) {
+    issue(kp, a.k.st, ko, kt, sm.sk[kt % NS]);
+    issue(vp, a.v.st, vo, kt, sm.sv[kt % NS]);
   };
 
   const Offs<D> off(l);
@@ -369,49 +379,120 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
+  auto needs_mask = [&](int kt) { return kt * kKB + kKB > wave_lim; };
+  // element r of a tile's scores is key kt*kKB + 8(r/4) + 4h + r%4
+  auto apply_mask = [&](f32x16& sv, int kt) {
+    const int rel = lim - kt * kKB - 4 * h;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = 8 * (r >> 2) + (r & 3) < rel ? sv[r] : -INFINITY;
+  };
+
+  // ---- prologue: tiles 0 .. NS-2 in flight, then S_0 and dP_0
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < n_kt) issue_tile(j, j);
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int cur = kt % NS;
-    wait_tiles<2 * C::NI>(min(NS - 2, n_kt - 1 - kt));
-    __syncthreads();
-    if (kt + NS - 1 < n_kt) issue_tile(kt + NS - 1, (kt + NS - 1) % NS);
-    const char* K = sk[cur];
-    const char* V = sv[cur];
-    const int k0 = kt * kTile;
-    const bool full = k0 + kTile <= wave_lim;
-    bf16x8 dsb[4];
+    if (j < n_kt) issue_tile(j);
+  wait_tiles<2 * NIQ>(min(NS - 2, n_kt - 1));
+  __syncthreads();
+  f32x16 sA = f32x16{}, dA = f32x16{}, sB, dB;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = f32x16{}, dpv = f32x16{};
+  for (int c = 0; c < C::NC; ++c) {
+    sA = mfma32(*(const bf16x8*)(sm.sk[0] + off.ro[c]), qf[c], sA);
+    dA = mfma32(*(const bf16x8*)(sm.sv[0] + off.ro[c]), df[c], dA);
+  }
+  if (needs_mask(0)) apply_mask(sA, 0);
+
+  // One tile u: `s`, `dp` hold S_u^T (masked) and dP_u^T; with NEXT, S_u+1 and dP_u+1 are
+  // formed into `sn`, `dpn`. Scheduling fences pin the MFMA / vector interleave.
+  auto step = [&](int u, f32x16& s, f32x16& dp, f32x16& sn, f32x16& dpn, auto next_tag)
+                  __attribute__((always_inline)) {
+    constexpr bool NEXT = decltype(next_tag)::value;
+    if constexpr (NEXT) wait_tiles<2 * NIQ>(min(NS - 3, n_kt - 2 - u));  // tile u+1 has landed
+    __syncthreads();  // tile u+1 visible; every wave is done with tile u-1
+    if (u + NS - 1 < n_kt) issue_tile(u + NS - 1);
+
+    // ---- phase A: dS_u = P_u (dP_u - delta) in bf16, with S_u+1 (and dP_u+1) on the matrix cores
+    constexpr bool DP_IN_A = D == 64;
+    constexpr int NM = (DP_IN_A ? 2 : 1) * C::NC;  // MFMAs of phase A (S and dP chains interleaved)
+    constexpr int EA = 16 / NM > 0 ? 16 / NM : 1;
+    constexpr int LA = D == 64 ? 4 : 2;  // operand reads in flight ahead of their MFMA
+    const char* kn = sm.sk[(u + 1) % NS];
+    const char* vn = sm.sv[(u + 1) % NS];
+    // operand j of phase A: K row chunk j (S only) or K / V row chunk j/2 (S and dP)
+    auto rd = [&](int j) {
+      if constexpr (DP_IN_A) return *(const bf16x8*)(((j & 1) ? vn : kn) + off.ro[j >> 1]);
+      else return *(const bf16x8*)(kn + off.ro[j]);
+    };
+    bf16x8 opa[LA];
+    if constexpr (NEXT) {
+      sn = f32x16{};
+      dpn = f32x16{};
+#pragma unroll
+      for (int j = 0; j < LA; ++j) opa[j] = rd(j);
+    }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int j = 0; j < NM; ++j) {
+      if constexpr (NEXT) {
+        if constexpr (DP_IN_A) {
+          if (j & 1) dpn = mfma32(opa[j % LA], df[j >> 1], dpn);
+          else sn = mfma32(opa[j % LA], qf[j >> 1], sn);
+        } else {
+          sn = mfma32(opa[j % LA], qf[j], sn);
+        }
+        if (j + LA < NM) opa[j % LA] = rd(j + LA);
+      }
+#pragma unroll
+      for (int e = 0; e < EA; ++e) {
+        const int r = EA * j + e;
+        if (r < 16) {
+          const float p = fast_exp2(fmaf(s[r], sl2, -lse2));
+          dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dl));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- phase B: dQ^T += K^T dS^T ; K^T operand rows = d, 8 keys 16t + 4h + {0..3}, +8
+    const char* K = sm.sk[u % NS];
+    bf16x8 kt8[C::NDB];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+      kt8[db] = cat8(lds_read_tr4((const __bf16*)(K + off.tro[0][db])), lds_read_tr4((const __bf16*)(K + off.tro[1][db])));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        acc[db] = mfma32(kt8[db], dsb[t], acc[db]);
+        if (t == 0)
+          kt8[db] = cat8(lds_read_tr4((const __bf16*)(K + 16 * C::ROWB + off.tro[0][db])),
+                         lds_read_tr4((const __bf16*)(K + 16 * C::ROWB + off.tro[1][db])));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if constexpr (NEXT && !DP_IN_A) {
+      bf16x8 vb[2];
+      vb[0] = *(const bf16x8*)(vn + off.ro[0]);
+      vb[1] = *(const bf16x8*)(vn + off.ro[1]);
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
-        s = mfma32(*(const bf16x8*)(K + 32 * kb * C::ROWB + off.ro[c]), qf[c], s);
-        dpv = mfma32(*(const bf16x8*)(V + 32 * kb * C::ROWB + off.ro[c]), df[c], dpv);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], sl2, -lse2));
-        if (!full) {
-          const int kk = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          p = kk < lim ? p : 0.f;
-        }
-        dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dpv[r] - dl));
+        dpn = mfma32(vb[c & 1], df[c], dpn);
+        if (c + 2 < C::NC) vb[c & 1] = *(const bf16x8*)(vn + off.ro[c + 2]);
       }
     }
-    // dQ^T += K^T dS^T ; K^T operand rows = d, 8 keys 16t + 4h + {0..3}, +8
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int rb = 16 * t * C::ROWB;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-        acc[db] = mfma32(cat8(lds_read_tr4((const __bf16*)(K + rb + off.tro[0][db])),
-                              lds_read_tr4((const __bf16*)(K + rb + off.tro[1][db]))),
-                         dsb[t], acc[db]);
-    }
+    if constexpr (NEXT)
+      if (needs_mask(u + 1)) apply_mask(sn, u + 1);
+  };
+
+  using T_ = std::integral_constant<bool, true>;
+  // Two tiles per trip so that the score registers alternate instead of being copied. The
+  // last tile also forms the scores of a tile past the end from a stale (in-bounds) LDS
+  // stage; they are never used, and one code path keeps the loop within the registers.
+  int u = 0;
+  for (; u + 1 < n_kt; u += 2) {
+    step(u, sA, dA, sB, dB, T_{});
+    step(u + 1, sB, dB, sA, dA, T_{});
   }
+  if (u < n_kt) step(u, sA, dA, sB, dB, T_{});
 
   if (row_ok) {
     float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
@@ -435,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
 }
 
 template <int D, int NS>
-__global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
   __shared__ DqLds<D, NS> sm;
   dq_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
 }
@@ -446,48 +527,45 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdArgs a, int n_qt) {
 // each alone is too small to. Workgroups are dealt to the 8 XCDs round-robin by
 // id, so both roles land on every XCD; within a role the ids are remapped as in
 // the single-role kernels.
-template <int D, int NS>
+template <int D, int NSK, int NSQ>
 __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_dq, int n_dq_pad) {
   __shared__ union {
-    DkdvLds<D, NS> kv;
-    DqLds<D, NS> q;
+    DkdvLds<D, NSK> kv;
+    DqLds<D, NSQ> q;
   } sm;
   const int id = blockIdx.x;
   if (id < n_dq_pad) {
     const int L = xcd_remap(id, n_dq_pad);
-    if (L < n_dq) dq_body<D, NS>(a, L, n_qt, sm.q);
+    if (L < n_dq) dq_body<D, NSQ>(a, L, n_qt, sm.q);
   } else {
-    dkdv_body<D, NS>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
+    dkdv_body<D, NSK>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
   }
 }
 
-#ifndef CPATTN_BWD_NS128
-#define CPATTN_BWD_NS128 2
-#endif
-
 template <int D>
 hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
-  constexpr int NS = D == 64 ? 4 : CPATTN_BWD_NS128;
+  constexpr int NSK = D == 64 ? 4 : 2;  // dK/dV: stages of 64 query rows
+  constexpr int NSQ = 4;                // dQ: stages of 32 keys
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;
   if constexpr (D == 64) {
     // both kernels keep two workgroups per CU at this width, so one grid costs nothing
     if (which == 3) {
-    const int64_t n_dq = bh * n_qt, n_dq_pad = (n_dq + 7) / 8 * 8;
-    const int64_t grid = n_dq_pad + bh * n_kt;
-    hipLaunchKernelGGL((bwd_fused_kernel<D, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt, n_qt,
-                       (int)n_dq, (int)n_dq_pad);
-    return hipGetLastError();
+      const int64_t n_dq = bh * n_qt, n_dq_pad = (n_dq + 7) / 8 * 8;
+      const int64_t grid = n_dq_pad + bh * n_kt;
+      hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
+                         n_qt, (int)n_dq, (int)n_dq_pad);
+      return hipGetLastError();
     }
   }
   if (which & 1) {
-    hipLaunchKernelGGL((dkdv_kernel<D, NS>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
-    hipLaunchKernelGGL((dq_kernel<D, NS>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
+    hipLaunchKernelGGL((dq_kernel<D, NSQ>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
     return hipGetLastError();
   }
   return hipSuccess;
