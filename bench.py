@@ -9,8 +9,9 @@ degree 4; bf16 inputs, fp32 accumulation), with every KV block resident in HBM:
     (cpattn_step_rows), block forward of the visible rows (step 0 straight into
     the accumulator), LSE merge of those rows (steps >= 1);
   * backward preprocess delta = rowsum(dO * O);
-  * for each ring step: dK/dV kernel then dQ kernel, accumulating in fp32
-    (accumulators cleared once at the start of the step).
+  * for each ring step: the block backward (cpattn_block_bwd: dK/dV and dQ
+    halves in one grid at D = 64), accumulating in fp32 (accumulators cleared
+    once at the start of the step).
 
 Throughput is causal-effective: only visible (query, key) pairs count, at
 4*D flops per pair for the forward and 10*D for the backward. Every launch of
@@ -20,6 +21,14 @@ CPU oracle is timed on a bounded sample of the same workload for the
 cpu_baseline object.
 
 Prints ONE JSON line. Only one GPU is supported.
+
+Two helper modes serve the roofline's measured HBM traffic:
+  --pmc-run      a few eager steps, then a plain 512 MiB device-to-device copy,
+                 to run under rocprofv3 --pmc FETCH_SIZE (and again WRITE_SIZE);
+  --traffic-from FETCH_CSV WRITE_CSV
+                 turns the two counter-collection CSVs into profiles/traffic.json:
+                 the dominant kernel's KiB per dispatch, each counter scaled by
+                 the bytes the copy moves over what that counter read for it.
 """
 from __future__ import annotations
 
@@ -45,6 +54,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
     ap.add_argument("--no-graph", action="store_true", help="time eager steps instead of graph replays")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="counter-collection run: eager steps, then the calibration copy")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic file from two rocprofv3 counter-collection CSVs")
     ap.add_argument("--split-bwd", action="store_true",
                     help="call the two halves of the block backward separately (per-half timings)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -352,8 +365,91 @@ def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
                       f"{reps} repetition(s), {sec:.2f} s each", "seconds_per_step": sec}
 
 
+COPY_BYTES = 512 << 20  # calibration copy for the HBM counters (twice the last-level cache)
+# GPU kernels behind each timed launch name (one dispatch of each per launch)
+GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "block_fwd": ("fwd_bf16_kernel",
+               "fwd_rope_kernel"), "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
+               "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",)}
+
+
+def kernel_source_hash():
+    """Hash of every device source of the library: traffic measured on other code is void."""
+    import hashlib
+    d = os.path.join(ROOT, "context_causal_attention_cpattn_amd", "csrc")
+    hsh = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            hsh.update(f.encode())
+            hsh.update(open(os.path.join(d, f), "rb").read())
+    return hsh.hexdigest()[:16]
+
+
+def pmc_run(args):
+    """A few eager steps of the workload, then the calibration copy three times."""
+    import torch
+    from workloads import BY_NAME
+    w = BY_NAME[args.workload]
+    share = Share(w, seed_do=w.seed + 1000)
+    share.split_bwd = args.split_bwd
+    share.build_plan(True)
+    for _ in range(3):
+        share.step()
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_run": w.name, "copy_bytes": COPY_BYTES}))
+
+
+def _counter_rows(path):
+    import csv
+    rows = []
+    for r in csv.DictReader(open(path)):
+        name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+        val = float(r.get("Counter_Value") or r.get("Counter-Value"))
+        did = int(r.get("Dispatch_Id") or r.get("Dispatch-Id") or 0)
+        rows.append((did, name, val))
+    return sorted(rows)
+
+
+def traffic_from(args):
+    """profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of --pmc-run."""
+    from workloads import BY_NAME
+    w = BY_NAME[args.workload]
+    name = "block_bwd" if not args.split_bwd else "block_bwd_dkdv"
+    out = {"kernel": name, "workload": w.name, "source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+           "csv": [os.path.relpath(p, ROOT) for p in args.traffic_from]}
+    total = 0.0
+    for key, path in zip(("fetch", "write"), args.traffic_from):
+        rows = _counter_rows(path)
+        copies = [v for _, n, v in rows if "copyBuffer" in n][-3:]
+        if len(copies) < 3:
+            raise SystemExit(f"{path}: the three calibration copies are missing")
+        copy_kib = sum(copies) / len(copies)
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        per_launch_kib = 0.0
+        for kn in GPU_KERNELS[name]:
+            vals = [v for _, n, v in rows if kn + "<" in n]
+            if vals:
+                per_launch_kib += sum(vals) / len(vals)
+        out[key] = {"kib_per_launch": per_launch_kib, "copy_kib": copy_kib, "factor": factor,
+                    "bytes_per_launch": per_launch_kib * 1024.0 * factor}
+        total += per_launch_kib * 1024.0 * factor
+    out["bytes_per_launch"] = total
+    path = args.traffic
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        return traffic_from(args)
+    if args.pmc_run:
+        return pmc_run(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -371,7 +467,7 @@ def main():
     traffic = None
     try:
         tj = json.load(open(args.traffic))
-        if tj.get("kernel") == dom and tj.get("workload") == w.name:
+        if tj.get("kernel") == dom and tj.get("workload") == w.name and tj.get("source_hash") == kernel_source_hash():
             traffic = tj.get("bytes_per_launch")
     except Exception:
         pass
