@@ -91,8 +91,12 @@ class Share:
         Tl = w.local_len
         self.tab = None
         if w.rope_theta:
+            # rotary: Q is rotated once per step and each K block once per ring step
+            # (cpattn_rope_rotate), then the blocks run without rotation
             self.tab = torch.empty(w.T, w.D, device=dev)
             cp.cpattn_rope_table(w.rope_theta, w.T, w.D, self.tab)
+            self.q_rot = torch.empty_like(self.q)
+            self.k_rot = torch.empty_like(self.kb[0])
         f32 = dict(device=dev, dtype=torch.float32)
         self.o = torch.empty(w.B, w.H, Tl, w.D, **f32)
         self.lse = torch.empty(w.B, w.H, Tl, **f32)
@@ -132,23 +136,37 @@ class Share:
         o, lse, ob, lb = T(self.o), T(self.lse, 3), T(self.o_blk), T(self.l_blk, 3)
         delta, dq = T(self.delta, 3), T(self.dq)
         qm = cp._map(self.maps[0])
-        rope = (None, 0) if self.tab is None else (cp.ctypes.c_void_p(self.tab.data_ptr()), self.tab.shape[0])
         by = cp.ctypes.byref
         keep = [q, do, o, lse, ob, lb, delta, dq, qm]
         plan = []
+        qf = q
+        if self.tab is not None:
+            tab, rows = cp.ctypes.c_void_p(self.tab.data_ptr()), self.tab.shape[0]
+            qf, kr = T(self.q_rot), T(self.k_rot)
+            keep += [qf, kr]
+            # x read + out written (bf16), the table row of each position once
+            rot_bytes = B * H * Tl * 4 * D + Tl * 4 * D
+            plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
+                         (by(q), bf16, B, H, Tl, D, by(qm), tab, rows, by(qf), st)))
         for s, (src, rb, pairs) in enumerate(self.steps):
             if rb >= Tl:
                 continue
             k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
             keep += [k, v, km]
+            if self.tab is not None:
+                plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
+                             (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
+                k = kr
             oo, ll = (o, lse) if s == 0 else (ob, lb)
             plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd,
-                         (by(q), by(k), by(v), bf16, B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, rope[0], rope[1],
+                         (by(qf), by(k), by(v), bf16, B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, None, 0,
                           0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
             if s > 0:
                 plan.append(("lse_merge", (Tl - rb) * self.bh * (12 * D + 12), lib.cpattn_lse_merge,
                              (by(o), by(lse), by(ob), by(lb), B, H, Tl, D, rb, Tl, st)))
         if do_bwd:
+            if self.tab is not None:
+                raise ValueError("the backward of the rotary workload is not part of this benchmark")
             plan.append(("bwd_preprocess", self.bh * Tl * (D * 2 + D * 4 + 4), lib.cpattn_bwd_preprocess,
                          (by(do), bf16, by(o), by(delta), B, H, Tl, D, st)))
             for src, rb, pairs in self.steps:
@@ -210,7 +228,7 @@ class EventLog:
     """HIP events around each launch on torch's current stream (the library's stream)."""
 
     BOUND = {"block_fwd": "mfma", "block_bwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma",
-             "lse_merge": "hbm", "bwd_preprocess": "hbm"}
+             "lse_merge": "hbm", "bwd_preprocess": "hbm", "rope_rotate": "hbm"}
 
     def __init__(self):
         self.rec = []
@@ -369,7 +387,8 @@ COPY_BYTES = 512 << 20  # calibration copy for the HBM counters (twice the last-
 # GPU kernels behind each timed launch name (one dispatch of each per launch)
 GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "block_fwd": ("fwd_bf16_kernel",
                "fwd_rope_kernel"), "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
-               "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",)}
+               "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",),
+               "rope_rotate": ("rope_rotate_kernel",)}
 
 
 def kernel_source_hash():

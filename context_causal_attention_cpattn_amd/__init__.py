@@ -21,7 +21,8 @@ from typing import Sequence
 
 __all__ = [
     "CpattnError", "lib_path", "load", "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard",
-    "cpattn_rope_table", "cpattn_block_fwd", "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes",
+    "cpattn_rope_table", "cpattn_rope_rotate", "cpattn_block_fwd", "cpattn_lse_merge",
+    "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
     "cpattn_step_rows", "EXPORTS",
 ]
@@ -34,7 +35,7 @@ CPATTN_F32, CPATTN_BF16 = 0, 1
 EXPORTS = (
     "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
-    "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows",
+    "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
 )
 
 
@@ -65,7 +66,8 @@ _SIGS = {
                                         _i64, _i64, _i64, _T, _T, _vp]),
     "cpattn_lse_merge": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _i64, _vp]),
     "cpattn_step_rows": (ctypes.c_int, [_M, _M, _i32, _P(_i64), _P(_i64)]),
-    "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64]),
+    "cpattn_rope_rotate": (ctypes.c_int, [_T, _i32, _i64, _i64, _i64, _i64, _M, _vp, _i64, _T, _vp]),
+    "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, ctypes.c_int32]),
     "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
     "cpattn_bwd_preprocess": (ctypes.c_int, [_T, _i32, _T, _T, _i64, _i64, _i64, _i64, _vp]),
@@ -188,8 +190,18 @@ def cpattn_step_rows(qmap, kmap, causal: bool = True):
     return rb.value, nk.value
 
 
-def cpattn_ring_fwd_workspace_bytes(B: int, H: int, Tq: int, D: int) -> int:
-    return int(load().cpattn_ring_fwd_workspace_bytes(B, H, Tq, D))
+def cpattn_ring_fwd_workspace_bytes(B: int, H: int, Tq: int, D: int, Tk: int | None = None, rope: bool = False) -> int:
+    return int(load().cpattn_ring_fwd_workspace_bytes(B, H, Tq, Tq if Tk is None else Tk, D, int(bool(rope))))
+
+
+def cpattn_rope_rotate(x, qmap, rope_table, out=None, stream=None):
+    """out (default: x itself) = x rotated row by row at the global positions of ``qmap``."""
+    B, H, T, D = x.shape
+    out = x if out is None else out
+    rp, rr = _rope_args(rope_table)
+    _check(load().cpattn_rope_rotate(_tensor(x), _dtype(x), B, H, T, D, _map(qmap), rp, rr, _tensor(out),
+                                     _stream(stream)))
+    return out
 
 
 def cpattn_ring_fwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, o_acc, lse_acc,

@@ -165,6 +165,28 @@ int cpattn_rope_table(double theta, int64_t rows, int64_t D, float* table, void*
   return launch_status(launch_rope_table(theta, (int)rows, (int)D, table, (hipStream_t)stream), "rope_table");
 }
 
+int cpattn_rope_rotate(const cpattn_tensor* x, int32_t dtype, int64_t B, int64_t H, int64_t T, int64_t D,
+                       const cpattn_posmap* map, const float* rope_table, int64_t rope_rows,
+                       const cpattn_tensor* out, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, T, T, D))) return st;
+  if (dtype != CPATTN_BF16) return fail(CPATTN_EUNSUPPORTED, "rotation of dtype %d (bf16 only)", (int)dtype);
+  if ((st = check_tensor(x, "x", 2)) || (st = check_tensor(out, "out", 2))) return st;
+  if ((st = check_map(map, T, "map"))) return st;
+  if (!rope_table || ((uintptr_t)rope_table & 15u) != 0) return fail(CPATTN_EINVAL, "rope table null or misaligned");
+  if (rope_rows <= 0 || rope_rows > kIntMax) return fail(CPATTN_EINVAL, "rope_rows");
+  if (max_pos(map) >= rope_rows)
+    return fail(CPATTN_EINVAL, "a global position is outside the rotary table (%lld rows)", (long long)rope_rows);
+  RotArgs a{};
+  a.x = view(x);
+  a.out = (__bf16*)out->data;
+  a.o_sb = out->sb, a.o_sh = out->sh, a.o_st = out->st;
+  a.B = (int)B, a.H = (int)H, a.T = (int)T, a.D = (int)D;
+  a.map = to_map(map);
+  a.table = rope_table;
+  return launch_status(launch_rope_rotate(a, (hipStream_t)stream), "rope_rotate");
+}
+
 int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
                      int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
                      const cpattn_posmap* kmap, int32_t causal, float scale, const float* rope_table,
@@ -217,11 +239,15 @@ int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32
   return ok();
 }
 
-size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D) {
-  if (B <= 0 || H <= 0 || Tq <= 0 || D <= 0) return 0;
-  const size_t o = (size_t)B * H * Tq * D * 4;
-  const size_t l = (size_t)B * H * Tq * 4;
-  return ((o + 255) / 256) * 256 + ((l + 255) / 256) * 256;
+// Workspace layout: [fp32 block O][fp32 block LSE] and, with a rotary table,
+// [rotated Q][rotated K block] in bf16; every part 256-byte aligned.
+static size_t ws_part(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t rope) {
+  if (B <= 0 || H <= 0 || Tq <= 0 || Tk <= 0 || D <= 0) return 0;
+  size_t n = ws_part((size_t)B * H * Tq * D * 4) + ws_part((size_t)B * H * Tq * 4);
+  if (rope) n += ws_part((size_t)B * H * Tq * D * 2) + ws_part((size_t)B * H * Tk * D * 2);
+  return n;
 }
 
 int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const cpattn_tensor* v_blocks,
@@ -240,17 +266,38 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
                         rope_table, rope_rows, 0, Tq, o_acc, lse_acc)))
       return st;
   }
-  const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Tq, D);
-  if (ring > 1) {
+  // With a rotary table and bf16 inputs, Q is rotated once and each K block once per
+  // step into the workspace, and the blocks run without rotation: every key is then
+  // rotated once instead of once per query tile.
+  const bool pre = rope_table != nullptr && dtype == CPATTN_BF16;
+  const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Tq, Tk, D, pre ? 1 : 0);
+  if (ring > 1 || pre) {
     if (!workspace || workspace_bytes < need)
       return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
     if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");
   }
-  float* o_ws = (float*)workspace;
-  float* l_ws = (float*)((char*)workspace + ((size_t)B * H * Tq * D * 4 + 255) / 256 * 256);
+  char* wp = (char*)workspace;
+  float* o_ws = (float*)wp;
+  float* l_ws = (float*)(wp + ws_part((size_t)B * H * Tq * D * 4));
+  __bf16* q_rot = (__bf16*)(wp + ws_part((size_t)B * H * Tq * D * 4) + ws_part((size_t)B * H * Tq * 4));
+  __bf16* k_rot = (__bf16*)((char*)q_rot + ws_part((size_t)B * H * Tq * D * 2));
   cpattn_tensor o_blk{o_ws, H * Tq * D, Tq * D, D};
   cpattn_tensor l_blk{l_ws, H * Tq, Tq, 1};
+  const cpattn_tensor q_r{q_rot, H * Tq * D, Tq * D, D};
+  const cpattn_tensor k_r{k_rot, H * Tk * D, Tk * D, D};
   hipStream_t s = (hipStream_t)stream;
+  if (pre) {
+    if ((st = cpattn_rope_rotate(q, dtype, B, H, Tq, D, qmap, rope_table, rope_rows, &q_r, stream))) return st;
+    q = &q_r;
+  }
+  const float* blk_rope = pre ? nullptr : rope_table;
+  // the K block a step uses: rotated into the workspace first when pre-rotating
+  auto key_block = [&](int32_t src) -> const cpattn_tensor* {
+    if (!pre) return &k_blocks[src];
+    if (cpattn_rope_rotate(&k_blocks[src], dtype, B, H, Tk, D, &kmaps[src], rope_table, rope_rows, &k_r, stream))
+      return nullptr;
+    return &k_r;
+  };
   for (int32_t step = 0; step < ring; ++step) {
     const int32_t src = ((rank - step) % ring + ring) % ring;
     const cpattn_posmap* km = &kmaps[src];
@@ -258,17 +305,21 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
     if ((st = cpattn_step_rows(qmap, km, causal, &rb, &nvis))) return st;
     if (step == 0) {
       // step 0 fills every row of the accumulator (rows without a visible key get O = 0, LSE = -inf)
+      const cpattn_tensor* kb = key_block(src);
+      if (!kb) return CPATTN_EHIP;
       FwdArgs a{};
-      build_fwd(a, q, &k_blocks[src], &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, rope_table,
-                rope_rows, 0, Tq, o_acc, lse_acc);
+      build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, blk_rope, rope_rows, 0, Tq,
+                o_acc, lse_acc);
       hipError_t e = dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
       if (e != hipSuccess) return launch_status(e, "ring_fwd step 0");
       continue;
     }
     if (rb >= Tq) continue;  // the whole block is in the future of every local row
+    const cpattn_tensor* kb = key_block(src);
+    if (!kb) return CPATTN_EHIP;
     FwdArgs a{};
-    build_fwd(a, q, &k_blocks[src], &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, rope_table,
-              rope_rows, rb, Tq, &o_blk, &l_blk);
+    build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, blk_rope, rope_rows, rb, Tq,
+              &o_blk, &l_blk);
     hipError_t e = dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
     if (e != hipSuccess) return launch_status(e, "ring_fwd block");
     MergeArgs m{};

@@ -74,4 +74,15 @@ hipError_t launch_bwd_preprocess(const PreArgs& a, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int which, hipStream_t s);
 hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStream_t s);
 
+// Rotation of bf16 rows at global positions into a (possibly aliasing) output.
+struct RotArgs {
+  View x;
+  __bf16* out;
+  int64_t o_sb, o_sh, o_st;
+  int B, H, T, D;
+  PosMap map;
+  const float* table;  // [rows][D/2][2]
+};
+hipError_t launch_rope_rotate(const RotArgs& a, hipStream_t s);
+
 }  // namespace cpattn

@@ -9,6 +9,8 @@
 // all lanes that share the row (one cache line per wave). Bytes per row:
 // 3 * 4D (two O reads, one O write) + 12 (two LSE reads, one write).
 
+#include <algorithm>
+
 #include "internal.h"
 
 namespace cpattn {
@@ -149,6 +151,54 @@ hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStr
   int64_t blocks = (n + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s, theta, rows, D, table);
+  return hipGetLastError();
+}
+
+// Rotary embedding of one [B,H,T,D] bf16 tensor at the global positions of its
+// rows: (x_i, x_{i+D/2}) -> (x_i cos - x_{i+D/2} sin, x_{i+D/2} cos + x_i sin),
+// angle from the table row of the position (half-split pairing), fp32
+// arithmetic, bf16 result rounded to nearest even. One thread rotates 8 pairs:
+// two 16-byte loads of x, four of the table, two 16-byte stores. Each thread
+// reads its elements before writing them, so out may alias x.
+namespace {
+__global__ __launch_bounds__(256) void rope_rotate_kernel(RotArgs a, int64_t n) {
+  typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  const int per_row = a.D / 16;  // threads per row
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n; g += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(g % per_row);
+    const int64_t rowid = g / per_row;
+    const int t = (int)(rowid % a.T);
+    const int64_t bh = rowid / a.T;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    const __bf16* xr = (const __bf16*)a.x.p + b * a.x.sb + h * a.x.sh + (int64_t)t * a.x.st;
+    __bf16* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)t * a.o_st;
+    const bf16x8 x1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 8 * c));
+    const bf16x8 x2 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + a.D / 2 + 8 * c));
+    const f32x4* tb = (const f32x4*)(a.table + (int64_t)a.map.pos(t) * a.D + 16 * c);
+    f32x4 cs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cs[j] = tb[j];
+    bf16x8 y1, y2;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float co = cs[e / 2][2 * (e % 2)], si = cs[e / 2][2 * (e % 2) + 1];
+      const float f1 = (float)x1[e], f2 = (float)x2[e];
+      y1[e] = (__bf16)(f1 * co - f2 * si);
+      y2[e] = (__bf16)(f2 * co + f1 * si);
+    }
+    *(u32x4*)(orow + 8 * c) = __builtin_bit_cast(u32x4, y1);
+    *(u32x4*)(orow + a.D / 2 + 8 * c) = __builtin_bit_cast(u32x4, y2);
+  }
+}
+}  // namespace
+
+hipError_t launch_rope_rotate(const RotArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.H * a.T * (a.D / 16);
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(rope_rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 1
+#define CPATTN_ABI_VERSION 2
 
 enum {
   CPATTN_OK = 0,
@@ -105,6 +105,23 @@ int cpattn_headtail_shard(int64_t T, int32_t ring, int32_t rank,
  * Errors: EINVAL if theta <= 0, rows <= 0, D odd or <= 0, table NULL.
  */
 int cpattn_rope_table(double theta, int64_t rows, int64_t D, float* table, void* stream);
+
+/*
+ * Rotary embedding applied once: out = x with every row i of every (b, h)
+ * rotated by the table row of its global position map(i), half-split pairs
+ * (i, i + D/2), fp32 arithmetic, bf16 result rounded to nearest even - the
+ * rotation the fused path of cpattn_block_fwd applies to q and k rows. A block
+ * rotated this way at its owner's positions can travel the ring as is, and the
+ * rotation is paid once per key instead of once per query tile.
+ *   x, out      [B,H,T,D] bf16; out may be x itself (in place)
+ *   rope_table  device table of cpattn_rope_table, rope_rows rows
+ * Errors: EINVAL for null or misaligned tensors or table, a map whose len
+ * differs from T, positions outside the table; EUNSUPPORTED for fp32 or D not
+ * in {64, 128}.
+ */
+int cpattn_rope_rotate(const cpattn_tensor* x, int32_t dtype, int64_t B, int64_t H, int64_t T,
+                       int64_t D, const cpattn_posmap* map, const float* rope_table,
+                       int64_t rope_rows, const cpattn_tensor* out, void* stream);
 
 /*
  * Block forward: attention of local query rows [row_begin, row_end) of q
@@ -158,8 +175,13 @@ int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc,
 int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
                      int64_t* row_begin, int64_t* visible_keys);
 
-/* Workspace bytes cpattn_ring_fwd needs: an fp32 block output and LSE. */
-size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t D);
+/*
+ * Workspace bytes cpattn_ring_fwd needs: an fp32 block output and LSE, and
+ * with rope != 0 (a rotary table with bf16 inputs) room for the rotated Q and
+ * one rotated K block. 0 for non-positive sizes.
+ */
+size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
+                                       int32_t rope);
 
 /*
  * Ring forward of rank `rank` out of `ring`, all KV blocks resident in HBM.
@@ -169,9 +191,13 @@ size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t
  * writes (o_acc, lse_acc) directly; every later step runs the block forward
  * on the rows that see at least one key of that block, into the workspace,
  * then merges those rows. Steps whose block is invisible to every row are
- * skipped. At most two launches per step, no synchronisation.
- * workspace: device memory of cpattn_ring_fwd_workspace_bytes(B,H,Tq,D)
- * bytes, 256-byte aligned. Other arguments as in cpattn_block_fwd.
+ * skipped. At most two launches per step, no synchronisation. With a rotary
+ * table and bf16 inputs, Q is rotated once (cpattn_rope_rotate) and each step
+ * first rotates its K block into the workspace, then runs the block without
+ * rotation (one more launch per step).
+ * workspace: device memory of cpattn_ring_fwd_workspace_bytes(B,H,Tq,Tk,D,
+ * rope) bytes, 256-byte aligned; may be NULL when ring == 1 without rotary.
+ * Other arguments as in cpattn_block_fwd.
  * Errors: as cpattn_block_fwd, plus EINVAL for ring < 1, rank out of range,
  * a short workspace.
  */

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 1
+    assert cp.cpattn_version() == 2
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -117,6 +117,35 @@ def test_ring_fwd_rejects():
 def test_ring_workspace_size():
     assert cp.cpattn_ring_fwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 128 * 4 + 32 * 8192 * 4
     assert cp.cpattn_ring_fwd_workspace_bytes(0, 1, 1, 1) == 0
+    # with rotary: rotated Q and one rotated K block in bf16, each part 256-byte aligned
+    base = cp.cpattn_ring_fwd_workspace_bytes(1, 16, 16384, 128)
+    assert cp.cpattn_ring_fwd_workspace_bytes(1, 16, 16384, 128, rope=True) == base + 2 * 16 * 16384 * 128 * 2
+    assert cp.cpattn_ring_fwd_workspace_bytes(1, 1, 3, 64, Tk=5, rope=True) == 768 + 256 + 512 + 768
+
+
+def test_ring_fwd_rotary_needs_workspace_even_alone():
+    lib = cp.load()
+    ks = (cp.cpattn_tensor * 1)(_t())
+    ms = (cp.cpattn_posmap * 1)(cp.cpattn_posmap(64, 32, 0, 0))
+    qm = cp.cpattn_posmap(64, 32, 0, 0)
+    o, lse = _t(), _t(st=1)
+    st = lib.cpattn_ring_fwd(ctypes.byref(_t()), ks, ks, ms, 1, 0, ctypes.byref(qm), 1, 1, 1, 64, 64, 64, 1, 0.0,
+                             ctypes.c_void_p(0x20000), 64, ctypes.byref(o), ctypes.byref(lse), None, 0, None)
+    assert st == -1 and "workspace" in cp.cpattn_last_error()
+
+
+def test_rope_rotate_rejects():
+    lib = cp.load()
+    t = _t()
+    bt = ctypes.byref(t)
+    m = cp.cpattn_posmap(64, 32, 0, 64)
+    tab = ctypes.c_void_p(0x20000)
+    assert lib.cpattn_rope_rotate(bt, 0, 1, 1, 64, 64, ctypes.byref(m), tab, 256, bt, None) == -2  # fp32
+    assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 64, 96, ctypes.byref(m), tab, 256, bt, None) == -2  # D = 96
+    assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 64, 64, ctypes.byref(m), tab, 127, bt, None) == -1  # pos 127 > rows
+    assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 64, 64, ctypes.byref(m), None, 256, bt, None) == -1  # no table
+    assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 65, 64, ctypes.byref(m), tab, 256, bt, None) == -1  # len != T
+    assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 64, 64, ctypes.byref(m), tab, 128, None, None) == -1  # no output
 
 
 def test_merge_and_bwd_reject():

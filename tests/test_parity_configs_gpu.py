@@ -36,7 +36,8 @@ class Share:
         if rope:
             self.tab = torch.empty(w.T, w.D, device=DEV)
             cp.cpattn_rope_table(w.rope_theta, w.T, w.D, self.tab)
-        self.ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(w.B, w.H, Tl, w.D), dtype=torch.uint8, device=DEV)
+        self.ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(w.B, w.H, Tl, w.D, rope=rope), dtype=torch.uint8,
+                              device=DEV)
         self.o = torch.empty(w.B, w.H, Tl, w.D, device=DEV)
         self.lse = torch.empty(w.B, w.H, Tl, device=DEV)
 

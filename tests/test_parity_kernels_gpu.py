@@ -165,6 +165,61 @@ def test_block_fwd_rope(D):
     assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
+def test_rope_rotate_in_place_strided_and_against_oracle():
+    """One rotation at global positions (HeadTail rank 1 of 3): within one bf16 rounding of
+    the fp64 rotation of the same bf16 input; in place == out of place; strided == contiguous."""
+    T, N, r, D = 1200, 3, 1, 128
+    log(f"rope_rotate T={T} N={N} rank={r} D={D}")
+    m, pos = cp.cpattn_headtail_shard(T, N, r)
+    B, H, Tl = 2, 3, T // N
+    x, = draw_shape(B, H, Tl, D, torch.bfloat16, seed=77, n=1)
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    xd = x.to(DEV)
+    out = torch.empty_like(xd)
+    cp.cpattn_rope_rotate(xd, m, tab, out)
+    big = torch.zeros(B, H, Tl, 2 * D, dtype=torch.bfloat16, device=DEV)  # rows padded to 2D
+    xs = big[..., :D]
+    xs.copy_(xd)
+    cp.cpattn_rope_rotate(xs, m, tab)  # in place, strided
+    torch.cuda.synchronize()
+    assert torch.equal(xs, out)
+    assert (big[..., D:] == 0).all()
+    Y = orope.rope_apply(f64(x), np.asarray(pos), 10000.0)
+    got = f64(out)
+    err = np.abs(got - Y) - (np.abs(Y) * 2.0 ** -8 + 1e-30)
+    log(f"  max err {np.abs(got - Y).max():.3g} (bound: one bf16 ulp)")
+    assert (err <= 0).all()
+
+
+@pytest.mark.parametrize("T,N,D", [(768, 3, 128), (512, 2, 64)])
+def test_ring_fwd_rope_all_ranks(T, N, D):
+    """Ring forward with a rotary table: Q and each K block rotated once, then plain blocks."""
+    log(f"ring_fwd rope T={T} N={N} D={D}")
+    B, H = 1, 2
+    q, k, v = draw_shape(B, H, T, D, torch.bfloat16, seed=T + 3 * N, n=3)
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, rr) for rr in range(N)])
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    Tl = T // N
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(B, H, Tl, D, rope=True), dtype=torch.uint8, device=DEV)
+    allpos = np.arange(T)
+    qr_, kr_ = orope.rope_apply(f64(q), allpos, 10000.0), orope.rope_apply(f64(k), allpos, 10000.0)
+    O, L = oa.causal_attention_fwd(qr_, kr_, f64(v))
+    for r in range(N):
+        o = torch.empty(B, H, Tl, D, device=DEV)
+        lse = torch.empty(B, H, Tl, device=DEV)
+        kb_before = [t.clone() for t in kb]
+        cp.cpattn_ring_fwd(gather(q, pos[r]), kb, vb, maps, r, maps[r], o, lse, ws, rope_table=tab)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(kb, kb_before))  # the K blocks are left as they were
+        eo, el = max_err(f64(o), O[:, :, list(pos[r])]), max_err(f64(lse), L[:, :, list(pos[r])])
+        log(f"  rank {r}: max err O {eo:.3g} LSE {el:.3g}")
+        assert eo <= TOL_BF16 and el <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------- ring forward
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
