@@ -3,7 +3,7 @@
  * load-balanced context parallelism, for AMD Instinct MI355X (gfx950).
  *
  * The operations follow the pages on context parallelism (BluScriptCP
- * development log, docs/Claude Logs.md):
+ * development log):
  *   - HeadTail shard map: entries of 2026-05-16 (chunk-level HeadTail) and
  *     2026-06-29 / 2026-07-10 (RopeDeltas.h: local index -> global position
  *     through a head delta and a tail delta);

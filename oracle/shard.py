@@ -1,6 +1,6 @@
 """HeadTail (load-balanced) shard map, written from its definition.
 
-Source: BluScriptCP development log (docs/Claude Logs.md).
+Source: BluScriptCP development log.
   * entry of 2026-05-16 on the HeadTail kernel: the permutation works on whole
     chunks, replacing the token-level interleave of the 2026-03-23 entry;
   * entry of 2026-06-29 on fused-RoPE load balancing: Megatron's per-rank
