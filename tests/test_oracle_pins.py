@@ -317,6 +317,59 @@ def test_bwd_finite_differences():
         assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name
 
 
+def _rope_loss(q, k, v, do, theta):
+    pos = np.arange(q.shape[-2])
+    O, _ = attention.causal_attention_fwd(rope.rope_apply(q, pos, theta), rope.rope_apply(k, pos, theta), v)
+    return float((O * do).sum())
+
+
+def test_rope_bwd_finite_differences():
+    """Backward through the rotary: central differences of sum(dO * O(Rq, Rk, v)) with
+    respect to the UNROTATED q, k, v (positions far apart so that every angle matters)."""
+    T, D, theta = 6, 8, 10.0
+    q, k, v, do = (rnd(T, D, seed=s) for s in (120, 121, 122, 123))
+    dq, dk, dv = rope.rope_attention_bwd(q, k, v, do, theta)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for i in range(T):
+            for d in range(D):
+                xp, xm = x.copy(), x.copy()
+                xp[i, d] += h
+                xm[i, d] -= h
+                args = {"q": q, "k": k, "v": v}
+                ap, am = dict(args), dict(args)
+                ap[name], am[name] = xp, xm
+                num[i, d] = (_rope_loss(ap["q"], ap["k"], ap["v"], do, theta) -
+                             _rope_loss(am["q"], am["k"], am["v"], do, theta)) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name
+
+
+def test_rope_transpose_is_the_inverse_rotation():
+    x = rnd(2, 7, 16, seed=124)
+    pos = np.array([0, 3, 17, 100, 4095, 9000, 32767])
+    y = rope.rope_apply(x, pos, 10000.0)
+    np.testing.assert_allclose(rope.rope_apply_transpose(y, pos, 10000.0), x, atol=1e-13)
+    # the transpose of a rotation by a is the rotation by -a
+    np.testing.assert_allclose(rope.rope_apply_transpose(x, pos, 10000.0), rope.rope_apply(x, -pos, 10000.0),
+                               atol=1e-13)
+    # and it preserves norms row by row
+    np.testing.assert_allclose(np.linalg.norm(rope.rope_apply_transpose(x, pos, 10000.0), axis=-1),
+                               np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+def test_mutant_rope_bwd_without_transpose_is_caught():
+    # planted: the q gradient rotated forward by R instead of back by R^T
+    T, D, theta = 6, 8, 10.0
+    q, k, v, do = (rnd(T, D, seed=s) for s in (125, 126, 127, 128))
+    pos = np.arange(T)
+    dqr, _, _, _, _ = attention.causal_attention_bwd(rope.rope_apply(q, pos, theta), rope.rope_apply(k, pos, theta),
+                                                     v, do)
+    bad = rope.rope_apply(dqr, pos, theta)
+    good, _, _ = rope.rope_attention_bwd(q, k, v, do, theta)
+    assert np.abs(bad - good).max() > 1e-3
+
+
 def test_bwd_matches_torch_autograd_float64():
     q, k, v, do = (torch.from_numpy(rnd(1, 2, 30, 8, seed=s)) for s in (84, 85, 86, 87))
     qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
