@@ -21,7 +21,7 @@ from typing import Sequence
 
 __all__ = [
     "CpattnError", "lib_path", "load", "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard",
-    "cpattn_rope_table", "cpattn_rope_rotate", "cpattn_block_fwd", "cpattn_lse_merge",
+    "cpattn_rope_table", "cpattn_rope_rotate", "cpattn_rope_rotate_grad", "cpattn_block_fwd", "cpattn_lse_merge",
     "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
     "cpattn_step_rows", "EXPORTS",
@@ -36,6 +36,7 @@ EXPORTS = (
     "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
+    "cpattn_rope_rotate_grad",
 )
 
 
@@ -67,6 +68,7 @@ _SIGS = {
     "cpattn_lse_merge": (ctypes.c_int, [_T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _i64, _vp]),
     "cpattn_step_rows": (ctypes.c_int, [_M, _M, _i32, _P(_i64), _P(_i64)]),
     "cpattn_rope_rotate": (ctypes.c_int, [_T, _i32, _i64, _i64, _i64, _i64, _M, _vp, _i64, _T, _vp]),
+    "cpattn_rope_rotate_grad": (ctypes.c_int, [_T, _i64, _i64, _i64, _i64, _M, _vp, _i64, _vp]),
     "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, ctypes.c_int32]),
     "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
@@ -202,6 +204,14 @@ def cpattn_rope_rotate(x, qmap, rope_table, out=None, stream=None):
     _check(load().cpattn_rope_rotate(_tensor(x), _dtype(x), B, H, T, D, _map(qmap), rp, rr, _tensor(out),
                                      _stream(stream)))
     return out
+
+
+def cpattn_rope_rotate_grad(g, qmap, rope_table, stream=None):
+    """In place: g (fp32, gradient with respect to rotated rows) <- R(pos)^T g."""
+    B, H, T, D = g.shape
+    rp, rr = _rope_args(rope_table)
+    _check(load().cpattn_rope_rotate_grad(_tensor(g), B, H, T, D, _map(qmap), rp, rr, _stream(stream)))
+    return g
 
 
 def cpattn_ring_fwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, o_acc, lse_acc,

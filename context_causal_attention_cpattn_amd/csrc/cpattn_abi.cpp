@@ -187,6 +187,25 @@ int cpattn_rope_rotate(const cpattn_tensor* x, int32_t dtype, int64_t B, int64_t
   return launch_status(launch_rope_rotate(a, (hipStream_t)stream), "rope_rotate");
 }
 
+int cpattn_rope_rotate_grad(const cpattn_tensor* g, int64_t B, int64_t H, int64_t T, int64_t D,
+                            const cpattn_posmap* map, const float* rope_table, int64_t rope_rows, void* stream) {
+  int st;
+  if ((st = check_dims(B, H, T, T, D))) return st;
+  if ((st = check_tensor(g, "g", 4))) return st;
+  if ((st = check_map(map, T, "map"))) return st;
+  if (!rope_table || ((uintptr_t)rope_table & 15u) != 0) return fail(CPATTN_EINVAL, "rope table null or misaligned");
+  if (rope_rows <= 0 || rope_rows > kIntMax) return fail(CPATTN_EINVAL, "rope_rows");
+  if (max_pos(map) >= rope_rows)
+    return fail(CPATTN_EINVAL, "a global position is outside the rotary table (%lld rows)", (long long)rope_rows);
+  RotGradArgs a{};
+  a.g = (float*)g->data;
+  a.sb = g->sb, a.sh = g->sh, a.st = g->st;
+  a.B = (int)B, a.H = (int)H, a.T = (int)T, a.D = (int)D;
+  a.map = to_map(map);
+  a.table = rope_table;
+  return launch_status(launch_rope_rotate_grad(a, (hipStream_t)stream), "rope_rotate_grad");
+}
+
 int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
                      int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
                      const cpattn_posmap* kmap, int32_t causal, float scale, const float* rope_table,

@@ -85,4 +85,14 @@ struct RotArgs {
 };
 hipError_t launch_rope_rotate(const RotArgs& a, hipStream_t s);
 
+// R(p)^T applied in place to fp32 gradient rows at global positions.
+struct RotGradArgs {
+  float* g;
+  int64_t sb, sh, st;
+  int B, H, T, D;
+  PosMap map;
+  const float* table;  // [rows][D/2][2]
+};
+hipError_t launch_rope_rotate_grad(const RotGradArgs& a, hipStream_t s);
+
 }  // namespace cpattn

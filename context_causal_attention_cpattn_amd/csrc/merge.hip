@@ -202,4 +202,44 @@ hipError_t launch_rope_rotate(const RotArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Backward through the rotary embedding: the gradient of the unrotated row is
+// R(p)^T times the gradient of the rotated row, i.e. the rotation by -a:
+// (g_i, g_{i+D/2}) -> (g_i cos + g_{i+D/2} sin, g_{i+D/2} cos - g_i sin), fp32
+// in place. One thread handles 4 pairs (16-byte loads and stores).
+namespace {
+__global__ __launch_bounds__(256) void rope_rotate_grad_kernel(RotGradArgs a, int64_t n) {
+  typedef __attribute__((ext_vector_type(4))) float f32x4;
+  const int per_row = a.D / 8;  // threads per row
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n; g += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(g % per_row);
+    const int64_t rowid = g / per_row;
+    const int t = (int)(rowid % a.T);
+    const int64_t bh = rowid / a.T;
+    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
+    float* row = a.g + b * a.sb + h * a.sh + (int64_t)t * a.st;
+    const f32x4 g1 = *(const f32x4*)(row + 4 * c);
+    const f32x4 g2 = *(const f32x4*)(row + a.D / 2 + 4 * c);
+    const f32x4* tb = (const f32x4*)(a.table + (int64_t)a.map.pos(t) * a.D + 8 * c);
+    const f32x4 t0 = tb[0], t1 = tb[1];
+    const float co[4] = {t0[0], t0[2], t1[0], t1[2]}, si[4] = {t0[1], t0[3], t1[1], t1[3]};
+    f32x4 y1, y2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y1[e] = g1[e] * co[e] + g2[e] * si[e];
+      y2[e] = g2[e] * co[e] - g1[e] * si[e];
+    }
+    *(f32x4*)(row + 4 * c) = y1;
+    *(f32x4*)(row + a.D / 2 + 4 * c) = y2;
+  }
+}
+}  // namespace
+
+hipError_t launch_rope_rotate_grad(const RotGradArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.H * a.T * (a.D / 8);
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(rope_rotate_grad_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, n);
+  return hipGetLastError();
+}
+
 }  // namespace cpattn

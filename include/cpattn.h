@@ -124,6 +124,20 @@ int cpattn_rope_rotate(const cpattn_tensor* x, int32_t dtype, int64_t B, int64_t
                        int64_t rope_rows, const cpattn_tensor* out, void* stream);
 
 /*
+ * Backward through the rotary embedding, in place: every row i of the fp32
+ * gradient g [B,H,T,D] with respect to ROTATED rows becomes the gradient with
+ * respect to the unrotated rows, R(p)^T g with p = map(i) (the rotation by the
+ * negated angle; each pair rotation is orthogonal). The rotation is linear, so
+ * a caller that ran the block backward on rotated q and k applies it once to
+ * the accumulated dQ and to each accumulated dK block after the last ring step.
+ * Errors: EINVAL for a null or misaligned g or table, a map whose len differs
+ * from T, positions outside the table; EUNSUPPORTED for D not in {64, 128}.
+ */
+int cpattn_rope_rotate_grad(const cpattn_tensor* g, int64_t B, int64_t H, int64_t T, int64_t D,
+                            const cpattn_posmap* map, const float* rope_table, int64_t rope_rows,
+                            void* stream);
+
+/*
  * Block forward: attention of local query rows [row_begin, row_end) of q
  * ([B,H,Tq,D]) against one KV block k, v ([B,H,Tk,D]) at global positions
  * qmap/kmap. Writes fp32 o [B,H,Tq,D] and lse [B,H,Tq] for those rows only.

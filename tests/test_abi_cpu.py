@@ -148,6 +148,18 @@ def test_rope_rotate_rejects():
     assert lib.cpattn_rope_rotate(bt, 1, 1, 1, 64, 64, ctypes.byref(m), tab, 128, None, None) == -1  # no output
 
 
+def test_rope_rotate_grad_rejects():
+    lib = cp.load()
+    t = _t()
+    bt = ctypes.byref(t)
+    m = cp.cpattn_posmap(64, 32, 0, 64)
+    tab = ctypes.c_void_p(0x20000)
+    assert lib.cpattn_rope_rotate_grad(bt, 1, 1, 64, 48, ctypes.byref(m), tab, 256, None) == -2  # D = 48
+    assert lib.cpattn_rope_rotate_grad(bt, 1, 1, 64, 64, ctypes.byref(m), tab, 100, None) == -1  # pos 127 >= rows
+    assert lib.cpattn_rope_rotate_grad(bt, 1, 1, 64, 64, ctypes.byref(m), ctypes.c_void_p(0x20004), 256, None) == -1
+    assert lib.cpattn_rope_rotate_grad(None, 1, 1, 64, 64, ctypes.byref(m), tab, 256, None) == -1
+
+
 def test_merge_and_bwd_reject():
     lib = cp.load()
     t, l3 = _t(), _t(st=1)

@@ -156,3 +156,79 @@ def test_bwd16k_all_ranks():
         ev = max_err(f64(dv[s.rank][:, heads]), dV[:, :, rows])
         log(f"  rank {s.rank}: O {eo:.3g} LSE {el:.3g} dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
         assert max(eo, el, eq, ek, ev) <= TOL_BF16
+
+
+def test_win32k_rope_backward_all_ranks_sampled():
+    """Backward through the rotary at the 32k window's full size (both ranks, all heads):
+    block backward on the rotated Q and K blocks, dQ and each dK block taken back through
+    R^T after the last step. The oracle checks sampled rows one by one: dQ of rows spread
+    over the sequence, dK and dV of the last keys (every query that sees them is in the last
+    rows); for every key, sum_j R(j) dK_j = 0 and sum_j dV_j = sum_p dO_p per head."""
+    w = BY_NAME["win32k"]
+    log(f"workload {w.name} backward through rotary")
+    g = torch.Generator().manual_seed(w.seed + 1000)
+    t = draw(w)
+    t["do"] = torch.randn(w.B, w.H, w.T, w.D, generator=g).to(torch.bfloat16)
+    N, Tl = w.ring, w.local_len
+    dk = [torch.zeros(w.B, w.H, Tl, w.D, device=DEV) for _ in range(N)]
+    dv = [torch.zeros_like(x) for x in dk]
+    shares = [Share(w, t, r, rope=True) for r in range(N)]
+    tab = shares[0].tab
+    kr = [cp.cpattn_rope_rotate(shares[0].kb[i], shares[0].maps[i], tab, torch.empty_like(shares[0].kb[i]))
+          for i in range(N)]
+    dq = []
+    for s in shares:
+        s.forward()
+        qrot = cp.cpattn_rope_rotate(s.q, s.maps[s.rank], tab, torch.empty_like(s.q))
+        delta = torch.empty(w.B, w.H, Tl, device=DEV)
+        cp.cpattn_bwd_preprocess(s.do, s.o, delta)
+        d = torch.zeros_like(s.o)
+        for st in range(N):
+            src = (s.rank - st) % N
+            cp.cpattn_block_bwd(qrot, kr[src], s.vb[src], s.do, s.lse, delta, d, dk[src], dv[src], s.maps[s.rank],
+                                s.maps[src])
+        cp.cpattn_rope_rotate_grad(d, s.maps[s.rank], tab)
+        dq.append(d)
+    for i in range(N):
+        cp.cpattn_rope_rotate_grad(dk[i], shares[0].maps[i], tab)
+    torch.cuda.synchronize()
+    T = w.T
+    where = {}
+    for r, s in enumerate(shares):
+        for li, gp in enumerate(s.pos[r]):
+            where[gp] = (r, li)
+    allpos = np.arange(T)
+    head = 9
+    q64, k64, v64, do64 = (f64(t[n][:, head:head + 1]) for n in ("q", "k", "v", "do"))
+    qr, krot = orope.rope_apply(q64, allpos, w.rope_theta), orope.rope_apply(k64, allpos, w.rope_theta)
+    # dQ of sampled rows
+    P = [0, 1, 777, T // 2 - 1, T // 2, 30000, T - 1]
+    O, L = oa.block_attention_fwd(qr[:, :, P], krot, v64, P, allpos)
+    gq, _, _ = oa.block_attention_bwd(qr[:, :, P], krot, v64, do64[:, :, P], O, L, P, allpos)
+    gq = orope.rope_apply_transpose(gq, P, w.rope_theta)
+    got = np.stack([f64(dq[where[p][0]][:, head:head + 1, where[p][1]]) for p in P], axis=2)
+    eq = max_err(got, gq)
+    # dK, dV of the last keys from the rows that can see them
+    J = [T - 68, T - 7, T - 1]
+    R = list(range(J[0], T))
+    O, L = oa.block_attention_fwd(qr[:, :, R], krot, v64, R, allpos)
+    _, gk, gv = oa.block_attention_bwd(qr[:, :, R], krot[:, :, J], v64[:, :, J], do64[:, :, R], O, L, R, J)
+    gk = orope.rope_apply_transpose(gk, J, w.rope_theta)
+    gotk = np.stack([f64(dk[where[j][0]][:, head:head + 1, where[j][1]]) for j in J], axis=2)
+    gotv = np.stack([f64(dv[where[j][0]][:, head:head + 1, where[j][1]]) for j in J], axis=2)
+    ek, ev = max_err(gotk, gk), max_err(gotv, gv)
+    log(f"  sampled rows, head {head}: dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
+    assert max(eq, ek, ev) <= TOL_BF16
+    # sums over every key of the sequence, all heads
+    kglob = np.zeros((w.B, w.H, T, w.D))
+    vglob = np.zeros_like(kglob)
+    for i in range(N):
+        kglob[:, :, list(shares[0].pos[i])] = f64(dk[i])
+        vglob[:, :, list(shares[0].pos[i])] = f64(dv[i])
+    ksum = orope.rope_apply(kglob, allpos, w.rope_theta).sum(axis=2)
+    kabs = np.abs(kglob).sum(axis=2)
+    vsum, dosum = vglob.sum(axis=2), f64(t["do"]).sum(axis=2)
+    rk = float((np.abs(ksum) / kabs).max())
+    rv = float((np.abs(vsum - dosum) / np.abs(vglob).sum(axis=2)).max())
+    log(f"  invariants: |sum R dK| / sum|dK| {rk:.3g}, |sum dV - sum dO| / sum|dV| {rv:.3g}")
+    assert rk <= 1e-3 and rv <= 1e-3

@@ -220,6 +220,77 @@ def test_ring_fwd_rope_all_ranks(T, N, D):
         assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
+def test_rope_rotate_grad_against_oracle_and_strided():
+    """R(p)^T of fp32 gradient rows at HeadTail positions, in place, against the fp64
+    transpose rotation; a row-strided view gives the same bits as a contiguous one."""
+    T, N, r, D = 1024, 2, 1, 64
+    log(f"rope_rotate_grad T={T} N={N} rank={r} D={D}")
+    m, pos = cp.cpattn_headtail_shard(T, N, r)
+    B, H, Tl = 2, 2, T // N
+    g = torch.Generator().manual_seed(91)
+    x = torch.randn(B, H, Tl, D, generator=g)
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    a = x.to(DEV)
+    cp.cpattn_rope_rotate_grad(a, m, tab)
+    big = torch.zeros(B, H, Tl, 2 * D, device=DEV)
+    bs = big[..., D:]
+    bs.copy_(x.to(DEV))
+    cp.cpattn_rope_rotate_grad(bs, m, tab)
+    torch.cuda.synchronize()
+    assert torch.equal(bs, a) and (big[..., :D] == 0).all()
+    Y = orope.rope_apply_transpose(f64(x), np.asarray(pos), 10000.0)
+    e = max_err(f64(a), Y)
+    log(f"  max err {e:.3g}")
+    assert e <= 2e-5
+
+
+@pytest.mark.parametrize("T,N,D", [(512, 2, 64), (768, 3, 128)])
+def test_ring_bwd_rope_all_ranks(T, N, D):
+    """Backward through the rotary: block backward on rotated Q / K blocks, then dQ and every
+    dK block taken back through R^T once after the last ring step."""
+    log(f"ring bwd rope T={T} N={N} D={D}")
+    B, H = 1, 2
+    q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=T + 5 * N, n=4)
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, r) for r in range(N)])
+    Tl = T // N
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    kr = [cp.cpattn_rope_rotate(kb[i], maps[i], tab, torch.empty_like(kb[i])) for i in range(N)]
+    ws = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(B, H, Tl, D, rope=True), dtype=torch.uint8, device=DEV)
+    dk = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(N)]
+    dv = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(N)]
+    gq = np.zeros((B, H, T, D))
+    for r in range(N):
+        qr, dor = gather(q, pos[r]), gather(do, pos[r])
+        o = torch.empty(B, H, Tl, D, device=DEV)
+        lse = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_ring_fwd(qr, kb, vb, maps, r, maps[r], o, lse, ws, rope_table=tab)
+        qrot = cp.cpattn_rope_rotate(qr, maps[r], tab, torch.empty_like(qr))
+        delta = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_bwd_preprocess(dor, o, delta)
+        dq = torch.zeros(B, H, Tl, D, device=DEV)
+        for s_ in range(N):
+            src = (r - s_) % N
+            cp.cpattn_block_bwd(qrot, kr[src], vb[src], dor, lse, delta, dq, dk[src], dv[src], maps[r], maps[src])
+        cp.cpattn_rope_rotate_grad(dq, maps[r], tab)
+        torch.cuda.synchronize()
+        gq[:, :, list(pos[r])] = f64(dq)
+    for i in range(N):
+        cp.cpattn_rope_rotate_grad(dk[i], maps[i], tab)
+    torch.cuda.synchronize()
+    gk, gv = np.zeros_like(gq), np.zeros_like(gq)
+    for i in range(N):
+        gk[:, :, list(pos[i])] = f64(dk[i])
+        gv[:, :, list(pos[i])] = f64(dv[i])
+    dQ, dK, dV = orope.rope_attention_bwd(f64(q), f64(k), f64(v), f64(do), 10000.0)
+    e = (max_err(gq, dQ), max_err(gk, dK), max_err(gv, dV))
+    log(f"  max err dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    assert max(e) <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------- ring forward
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
