@@ -165,8 +165,6 @@ class Share:
                 plan.append(("lse_merge", (Tl - rb) * self.bh * (12 * D + 12), lib.cpattn_lse_merge,
                              (by(o), by(lse), by(ob), by(lb), B, H, Tl, D, rb, Tl, st)))
         if do_bwd:
-            if self.tab is not None:
-                raise ValueError("the backward of the rotary workload is not part of this benchmark")
             plan.append(("bwd_preprocess", self.bh * Tl * (D * 2 + D * 4 + 4), lib.cpattn_bwd_preprocess,
                          (by(do), bf16, by(o), by(delta), B, H, Tl, D, st)))
             for src, rb, pairs in self.steps:
@@ -175,6 +173,11 @@ class Share:
                 k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
                 dk, dv = T(self.dk[src]), T(self.dv[src])
                 keep += [k, v, km, dk, dv]
+                if self.tab is not None:
+                    # backward over the rotated rows: rotate the block's keys again, Q stays rotated
+                    plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
+                                 (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
+                    k, q = kr, qf
                 if not split_bwd:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
@@ -186,6 +189,19 @@ class Share:
                 plan.append(("block_bwd_dq", 6 * D * pairs * self.bh, lib.cpattn_block_bwd_dq,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), B, H, Tl, Tk, D, by(qm),
                               by(km), 1, 0.0, st)))
+            if self.tab is not None:
+                # gradients back through R^T once: dQ, then every dK block (fp32 read and written,
+                # the table row of each position once)
+                gbytes = B * H * Tl * 8 * D + Tl * 4 * D
+                plan.append(("rope_rotate_grad", gbytes, lib.cpattn_rope_rotate_grad,
+                             (by(dq), B, H, Tl, D, by(qm), tab, rows, st)))
+                for src, rb, _ in self.steps:
+                    if rb >= Tl:
+                        continue
+                    dk, km = T(self.dk[src]), cp._map(self.maps[src])
+                    keep += [dk, km]
+                    plan.append(("rope_rotate_grad", gbytes, lib.cpattn_rope_rotate_grad,
+                                 (by(dk), B, H, Tk, D, by(km), tab, rows, st)))
         self._keep = keep
         self.plan = plan
         self.do_bwd = do_bwd
@@ -228,7 +244,7 @@ class EventLog:
     """HIP events around each launch on torch's current stream (the library's stream)."""
 
     BOUND = {"block_fwd": "mfma", "block_bwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma",
-             "lse_merge": "hbm", "bwd_preprocess": "hbm", "rope_rotate": "hbm"}
+             "lse_merge": "hbm", "bwd_preprocess": "hbm", "rope_rotate": "hbm", "rope_rotate_grad": "hbm"}
 
     def __init__(self):
         self.rec = []
@@ -388,7 +404,7 @@ COPY_BYTES = 512 << 20  # calibration copy for the HBM counters (twice the last-
 GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "block_fwd": ("fwd_bf16_kernel",
                "fwd_rope_kernel"), "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
                "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",),
-               "rope_rotate": ("rope_rotate_kernel",)}
+               "rope_rotate": ("rope_rotate_kernel",), "rope_rotate_grad": ("rope_rotate_grad_kernel",)}
 
 
 def kernel_source_hash():
@@ -522,12 +538,12 @@ def main():
             wx = BY_NAME[name]
             sx = Share(wx, seed_do=wx.seed + 1000)
             sx.split_bwd = True  # at D = 128 the two halves are separate launches anyway
-            bwd = name == "win16k"
+            bwd = True
             wl, kx, _ = time_steps(sx, 3, 1, do_bwd=bwd)
             fl = sx.flops(bwd)
             extra[name] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
                            "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
-                           "parts": "forward + backward" if bwd else "forward with rotary",
+                           "parts": "forward + backward" + (" with rotary" if wx.rope_theta else ""),
                            "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
                                            "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
             del sx
