@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, brute, merge, ring, rope, shard
+from oracle import attention, brute, gqa, merge, ring, rope, shard
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -368,6 +368,59 @@ def test_mutant_rope_bwd_without_transpose_is_caught():
     bad = rope.rope_apply(dqr, pos, theta)
     good, _, _ = rope.rope_attention_bwd(q, k, v, do, theta)
     assert np.abs(bad - good).max() > 1e-3
+
+
+def _gqa_loss(q, k, v, do):
+    T = q.shape[-2]
+    O, _ = gqa.block_attention_fwd(q, k, v, np.arange(T), np.arange(T))
+    return float((O * do).sum())
+
+
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (3, 1)])
+def test_gqa_bwd_finite_differences(H, H_kv):
+    """GQA / MQA: central differences of sum(dO * O) with respect to the SHARED K and V
+    heads (each feeds several query heads) and to Q."""
+    T, D = 5, 4
+    q, do = rnd(1, H, T, D, seed=130), rnd(1, H, T, D, seed=131)
+    k, v = rnd(1, H_kv, T, D, seed=132), rnd(1, H_kv, T, D, seed=133)
+    pos = np.arange(T)
+    o, lse = gqa.block_attention_fwd(q, k, v, pos, pos)
+    dq, dk, dv = gqa.block_attention_bwd(q, k, v, do, o, lse, pos, pos)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            ap, am = dict(args), dict(args)
+            ap[name], am[name] = xp, xm
+            num[idx] = (_gqa_loss(ap["q"], ap["k"], ap["v"], do) - _gqa_loss(am["q"], am["k"], am["v"], do)) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name
+
+
+def test_gqa_groups_are_consecutive_heads_and_g1_is_mha():
+    q, k, v = rnd(1, 6, 9, 8, seed=134), rnd(1, 2, 9, 8, seed=135), rnd(1, 2, 9, 8, seed=136)
+    pos = np.arange(9)
+    o, _ = gqa.block_attention_fwd(q, k, v, pos, pos)
+    # query heads 0..2 use KV head 0, heads 3..5 KV head 1 (brute force per head)
+    for h in range(6):
+        ob, _ = brute.attention(_tolist(q[0, h]), _tolist(k[0, h // 3]), _tolist(v[0, h // 3]), list(pos), list(pos))
+        np.testing.assert_allclose(o[0, h], np.array(ob), atol=1e-12)
+    k6, v6 = rnd(1, 6, 9, 8, seed=137), rnd(1, 6, 9, 8, seed=138)
+    o1, l1 = gqa.block_attention_fwd(q, k6, v6, pos, pos)
+    o2, l2 = attention.block_attention_fwd(q, k6, v6, pos, pos)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_mutant_gqa_strided_grouping_is_caught():
+    # planted: query head h paired with KV head h % H_kv instead of h // G
+    q, k, v = rnd(1, 4, 7, 8, seed=139), rnd(1, 2, 7, 8, seed=140), rnd(1, 2, 7, 8, seed=141)
+    pos = np.arange(7)
+    good, _ = gqa.block_attention_fwd(q, k, v, pos, pos)
+    bad, _ = attention.block_attention_fwd(q, np.tile(k, (1, 2, 1, 1)), np.tile(v, (1, 2, 1, 1)), pos, pos)
+    assert np.abs(good - bad).max() > 1e-3
 
 
 def test_bwd_matches_torch_autograd_float64():
