@@ -24,7 +24,7 @@ __all__ = [
     "cpattn_rope_table", "cpattn_rope_rotate", "cpattn_rope_rotate_grad", "cpattn_block_fwd", "cpattn_lse_merge",
     "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
-    "cpattn_step_rows", "EXPORTS",
+    "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +36,7 @@ EXPORTS = (
     "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
-    "cpattn_rope_rotate_grad",
+    "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa",
 )
 
 
@@ -69,6 +69,10 @@ _SIGS = {
     "cpattn_step_rows": (ctypes.c_int, [_M, _M, _i32, _P(_i64), _P(_i64)]),
     "cpattn_rope_rotate": (ctypes.c_int, [_T, _i32, _i64, _i64, _i64, _i64, _M, _vp, _i64, _T, _vp]),
     "cpattn_rope_rotate_grad": (ctypes.c_int, [_T, _i64, _i64, _i64, _i64, _M, _vp, _i64, _vp]),
+    "cpattn_block_fwd_gqa": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32, _f32,
+                                            _vp, _i64, _i64, _i64, _T, _T, _vp]),
+    "cpattn_block_bwd_gqa": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64,
+                                            _i64, _M, _M, _i32, _f32, _vp]),
     "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, ctypes.c_int32]),
     "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
@@ -264,3 +268,26 @@ def cpattn_block_bwd_dq(q, k, v, dout, lse, delta, dq_acc, qmap, kmap, causal: b
     _check(load().cpattn_block_bwd_dq(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                       _tensor(delta, 3), _tensor(dq_acc), B, H, Tq, Tk, D, _map(qmap), _map(kmap),
                                       int(causal), float(scale), _stream(stream)))
+
+
+def cpattn_block_fwd_gqa(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: float = 0.0, rope_table=None,
+                         row_begin: int = 0, row_end: int | None = None, stream=None):
+    """Grouped-query block forward: q [B,H,Tq,D], k / v [B,H_kv,Tk,D], query head h uses KV head h // (H // H_kv)."""
+    B, H, Tq, D = q.shape
+    H_kv, Tk = k.shape[1], k.shape[2]
+    rp, rr = _rope_args(rope_table)
+    row_end = Tq if row_end is None else row_end
+    _check(load().cpattn_block_fwd_gqa(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
+                                       _map(qmap), _map(kmap), int(causal), float(scale), rp, rr, row_begin, row_end,
+                                       _tensor(o), _tensor(lse, 3), _stream(stream)))
+
+
+def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
+                         scale: float = 0.0, stream=None):
+    """Grouped-query block backward: dk_acc / dv_acc per KV head, summed over each group."""
+    B, H, Tq, D = q.shape
+    H_kv, Tk = k.shape[1], k.shape[2]
+    _check(load().cpattn_block_bwd_gqa(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
+                                       _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H,
+                                       H_kv, Tq, Tk, D, _map(qmap), _map(kmap), int(causal), float(scale),
+                                       _stream(stream)))

@@ -93,24 +93,20 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const int bh = Lg / n_kt;
+  const int bh = Lg / n_kt;  // (b, KV head)
   const int kt = Lg - bh * n_kt;
-  const int b = bh / a.H, hh = bh - b * a.H;
+  const int H_kv = a.H / a.G;
+  const int b = bh / H_kv, kvh = bh - b * H_kv;
   const int kc0 = kt * kKeysPerWG;         // first key of the workgroup
   const int kw0 = kc0 + 32 * w;            // first key of the wave
   const int key = kw0 + lq;                // this lane's key
   const bool key_ok = key < a.Tk;
 
-  const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh;
-  const __bf16* dop = (const __bf16*)a.dout.p + b * a.dout.sb + hh * a.dout.sh;
-  const float* lp = (const float*)a.lse.p + b * a.lse.sb + hh * a.lse.sh;
-  const float* dp = (const float*)a.delta.p + b * a.delta.sb + hh * a.delta.sh;
-
   // K and V rows of this lane's key (B operands: column = key, 8 consecutive d)
   bf16x8 kf[C::NC], vf[C::NC];
   {
-    const __bf16* kk = (const __bf16*)a.k.p + b * a.k.sb + hh * a.k.sh + (int64_t)key * a.k.st;
-    const __bf16* vv = (const __bf16*)a.v.p + b * a.v.sb + hh * a.v.sh + (int64_t)key * a.v.st;
+    const __bf16* kk = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st;
+    const __bf16* vv = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
       u32x4 z = {0u, 0u, 0u, 0u};
@@ -131,6 +127,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   const int q_first = a.causal ? a.qm.count_lt(a.km.pos(kc0)) : 0;
   const int t_begin = q_first / kTile;
   const int t_end = (a.Tq + kTile - 1) / kTile;
+  const int n = t_end - t_begin;  // tiles per query head
+  const int n_items = n * a.G;    // (query head of the group, tile), head-major
   const float sl2 = a.scale * kLog2e;
 
   int ld_row[C::NI], ld_col[C::NI];
@@ -146,7 +144,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   // LSE and delta rows of a tile: every wave brings 16 of the 64 (lanes 0..15)
   const unsigned lo_lse = (unsigned)((16 * w + (l & 15)) * a.lse.st * 4);
   const unsigned lo_dl = (unsigned)((16 * w + (l & 15)) * a.delta.st * 4);
-  auto issue_tile = [&](int t, int buf) {
+  // item it = (query head kvh*G + it/n, tile t_begin + it%n)
+  auto issue_tile = [&](int it, int buf) {
+    const int hq = kvh * a.G + it / n;
+    const int t = t_begin + it % n;
+    const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hq * a.q.sh;
+    const __bf16* dop = (const __bf16*)a.dout.p + b * a.dout.sb + hq * a.dout.sh;
+    const float* lp = (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh;
+    const float* dp = (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
     const int q0 = t * kTile;
     const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
     const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
@@ -181,13 +186,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (t_begin + j < t_end) issue_tile(t_begin + j, j);
+    if (j < n_items) issue_tile(j, j);
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int cur = (t - t_begin) % NS;
-    wait_tiles<2 * C::NI + 2>(min(NS - 2, t_end - 1 - t));
+  // every query head of the group in turn: dK and dV sum over the group in registers
+  for (int it = 0; it < n_items; ++it) {
+    const int t = t_begin + it % n;
+    const int cur = it % NS;
+    wait_tiles<2 * C::NI + 2>(min(NS - 2, n_items - 1 - it));
     __syncthreads();
-    if (t + NS - 1 < t_end) issue_tile(t + NS - 1, (t - t_begin + NS - 1) % NS);
+    if (it + NS - 1 < n_items) issue_tile(it + NS - 1, (it + NS - 1) % NS);
     const char* Q = sq[cur];
     const char* DO = sdo[cur];
     const int q0 = t * kTile;
@@ -255,15 +262,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     }
   }
 
-  if (t_begin >= t_end) return;  // no query of this block sees these keys: nothing to add
+  if (n_items <= 0) return;  // no query of this block sees these keys: nothing to add
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) {
     mfma_agpr_drain(dk[db]);
     mfma_agpr_drain(dv[db]);
   }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j
-  float* dkp = a.dk + b * a.dk_sb + hh * a.dk_sh;
-  float* dvp = a.dv + b * a.dv_sb + hh * a.dv_sh;
+  float* dkp = a.dk + b * a.dk_sb + kvh * a.dk_sh;
+  float* dvp = a.dv + b * a.dv_sb + kvh * a.dv_sh;
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -324,8 +331,9 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
   const float sl2 = a.scale * kLog2e;
 
-  const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + hh * a.k.sh;
-  const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + hh * a.v.sh;
+  const int kvh = hh / a.G;  // the KV head of this query head's group
+  const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh;
+  const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh;
 
   // ---- Q and dO rows of this lane's query (B operands), LSE and delta of the row
   bf16x8 qf[C::NC], df[C::NC];
@@ -548,19 +556,20 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   constexpr int NSQ = 4;                // dQ: stages of 32 keys
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
-  const int64_t bh = (int64_t)a.B * a.H;
+  const int64_t bh = (int64_t)a.B * a.H;           // (b, query head) for dQ
+  const int64_t bkv = (int64_t)a.B * (a.H / a.G);  // (b, KV head) for dK / dV
   if constexpr (D == 64) {
     // both kernels keep two workgroups per CU at this width, so one grid costs nothing
     if (which == 3) {
       const int64_t n_dq = bh * n_qt, n_dq_pad = (n_dq + 7) / 8 * 8;
-      const int64_t grid = n_dq_pad + bh * n_kt;
+      const int64_t grid = n_dq_pad + bkv * n_kt;
       hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
                          n_qt, (int)n_dq, (int)n_dq_pad);
       return hipGetLastError();
     }
   }
   if (which & 1) {
-    hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bh * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -126,6 +126,15 @@ int build_fwd(FwdArgs& a, const cpattn_tensor* q, const cpattn_tensor* k, const 
   a.rope_rows = (int)rope_rows;
   a.row_begin = (int)row_begin;
   a.row_end = (int)row_end;
+  a.G = 1;
+  return CPATTN_OK;
+}
+
+// Query heads per KV head for H query heads sharing H_kv KV heads.
+int group_of(int64_t H, int64_t H_kv, int* G) {
+  if (H_kv <= 0 || H_kv > H || H % H_kv != 0)
+    return fail(CPATTN_EINVAL, "H = %lld is not a multiple of H_kv = %lld", (long long)H, (long long)H_kv);
+  *G = (int)(H / H_kv);
   return CPATTN_OK;
 }
 
@@ -217,6 +226,21 @@ int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
   if (st) return st;
   hipStream_t s = (hipStream_t)stream;
   return launch_status(dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s), "block_fwd");
+}
+
+int cpattn_block_fwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
+                         const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
+                         const float* rope_table, int64_t rope_rows, int64_t row_begin, int64_t row_end,
+                         const cpattn_tensor* o, const cpattn_tensor* lse, void* stream) {
+  FwdArgs a{};
+  int G;
+  int st = build_fwd(a, q, k, v, dtype, B, H, Tq, Tk, D, qmap, kmap, causal, scale, rope_table, rope_rows,
+                     row_begin, row_end, o, lse);
+  if (st || (st = group_of(H, H_kv, &G))) return st;
+  a.G = G;
+  hipStream_t s = (hipStream_t)stream;
+  return launch_status(dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s), "block_fwd_gqa");
 }
 
 int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, const cpattn_tensor* o_blk,
@@ -379,9 +403,10 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
                int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
                const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq,
                int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-               float scale, int which, void* stream, const char* what) {
-  int st;
+               float scale, int which, void* stream, const char* what, int64_t H_kv) {
+  int st, G;
   if ((st = check_dims(B, H, Tq, Tk, D))) return st;
+  if ((st = group_of(H, H_kv, &G))) return st;
   if (dtype == CPATTN_F32) return fail(CPATTN_EUNSUPPORTED, "block backward takes bf16 inputs");
   if (dtype != CPATTN_BF16) return fail(CPATTN_EINVAL, "dtype %d", (int)dtype);
   if ((st = check_tensor(q, "q", 2)) || (st = check_tensor(k, "k", 2)) || (st = check_tensor(v, "v", 2)) ||
@@ -404,6 +429,7 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
   a.qm = to_map(qmap), a.km = to_map(kmap);
   a.causal = causal != 0;
   a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
+  a.G = G;
   return launch_status(launch_bwd_bf16(a, which, (hipStream_t)stream), what);
 }
 
@@ -411,13 +437,23 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
 
 extern "C" {
 
+int cpattn_block_bwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                         const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                         const cpattn_tensor* delta, const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc,
+                         const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                         int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                         float scale, void* stream) {
+  return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
+                    scale, 3, stream, "block_bwd_gqa", H_kv);
+}
+
 int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                      const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
                      const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
                      int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
                      const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 3, stream, "block_bwd");
+                    scale, 3, stream, "block_bwd", H);
 }
 
 int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -426,7 +462,7 @@ int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const 
                           int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
                           const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, nullptr, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 1, stream, "block_bwd_dkdv");
+                    scale, 1, stream, "block_bwd_dkdv", H);
 }
 
 int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
@@ -435,7 +471,7 @@ int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cp
                         const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
                         void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, nullptr, nullptr, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 2, stream, "block_bwd_dq");
+                    scale, 2, stream, "block_bwd_dq", H);
 }
 
 }  // extern "C"

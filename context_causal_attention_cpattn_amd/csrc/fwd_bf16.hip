@@ -99,8 +99,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   const bool row_ok = row < a.row_end;
 
   const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh;
-  const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + hh * a.k.sh;
-  const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + hh * a.v.sh;
+  const int kvh = hh / a.G;  // the KV head of this query head's group
+  const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh;
+  const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh;
 
   // ---- Q fragment (B operand of S^T): lane holds Q[row][16c + 8h .. +7]
   bf16x8 qf[C::NC];

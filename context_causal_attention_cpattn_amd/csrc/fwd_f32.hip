@@ -32,8 +32,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, int n_qt) {
   const bool row_ok = row < a.row_end;
 
   const float* qp = (const float*)a.q.p + b * a.q.sb + hh * a.q.sh;
-  const float* kp = (const float*)a.k.p + b * a.k.sb + hh * a.k.sh;
-  const float* vp = (const float*)a.v.p + b * a.v.sb + hh * a.v.sh;
+  const int kvh = hh / a.G;  // the KV head of this query head's group
+  const float* kp = (const float*)a.k.p + b * a.k.sb + kvh * a.k.sh;
+  const float* vp = (const float*)a.v.p + b * a.v.sb + kvh * a.v.sh;
 
   float q[DQ], acc[DQ];
 #pragma unroll

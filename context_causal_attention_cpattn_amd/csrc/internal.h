@@ -26,6 +26,7 @@ struct FwdArgs {
   const float* rope;  // [rope_rows][D/2][2] or null
   int rope_rows;
   int row_begin, row_end;
+  int G;  // query heads per KV head: query head h reads K and V head h / G
 };
 
 struct MergeArgs {
@@ -63,6 +64,7 @@ struct BwdArgs {
   PosMap qm, km;
   int causal;
   float scale;
+  int G;  // query heads per KV head; dK / dV are per KV head, summed over its group
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

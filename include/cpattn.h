@@ -159,6 +159,22 @@ int cpattn_block_fwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
                      const cpattn_tensor* o, const cpattn_tensor* lse, void* stream);
 
 /*
+ * Grouped-query form of cpattn_block_fwd (GQA; MQA when H_kv = 1): q, o and
+ * lse have H heads, k and v H_kv heads, and query head h attends with KV head
+ * h / (H / H_kv) - the grouping of the BluScriptCP log (2026-07-06: query head
+ * hq uses KV head hq / G; 2026-06-29: the ring keeps the KV heads grouped, so
+ * blocks travel with H_kv heads only). Every other argument as in
+ * cpattn_block_fwd, which is this call with H_kv = H.
+ * Errors: as cpattn_block_fwd, plus EINVAL if H is not a multiple of H_kv.
+ */
+int cpattn_block_fwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                         int32_t dtype, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                         int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                         float scale, const float* rope_table, int64_t rope_rows,
+                         int64_t row_begin, int64_t row_end,
+                         const cpattn_tensor* o, const cpattn_tensor* lse, void* stream);
+
+/*
  * SDPAMerger: for rows [row_begin, row_end) of every (b, h), fold the block
  * result (o_blk, lse_blk) into the running result (o_acc, lse_acc), in place:
  *   L = log(exp(L_acc) + exp(L_blk)),
@@ -257,6 +273,23 @@ int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
                      int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
                      const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
                      float scale, void* stream);
+
+/*
+ * Grouped-query form of cpattn_block_bwd: q, dout, lse, delta and dq_acc have
+ * H heads; k, v, dk_acc and dv_acc have H_kv heads. Query head h reads KV head
+ * h / (H / H_kv); the gradient of a KV head adds the contributions of all its
+ * query heads, summed in fp32 registers by one workgroup before it is added to
+ * dk_acc / dv_acc (the group reduce of the BluScriptCP log, 2026-07-01; no
+ * atomics, bitwise reproducible). dQ stays per query head.
+ * Errors: as cpattn_block_bwd, plus EINVAL if H is not a multiple of H_kv.
+ */
+int cpattn_block_bwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                         const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                         const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
+                         const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
+                         const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                         float scale, void* stream);
 
 /*
  * The two halves of cpattn_block_bwd, same arguments and accumulate semantics:

@@ -9,7 +9,9 @@ Modules
   attention  full-sequence causal softmax attention and block attention at
              global positions, forward (O, LSE) and analytic backward
   merge      log-sum-exp merge of two partial results
-  rope       rotary position embedding at global positions
+  rope       rotary position embedding at global positions, and the backward
+             through it (the transposed rotation)
+  gqa        grouped-query attention: KV heads shared by groups of query heads
   brute      pure-Python loop versions for tiny inputs (independent cross-check)
   ring       the ring schedule assembled from the pieces above (used by the
              invariant tests: any chunk partition, any ring order)

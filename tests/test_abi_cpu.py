@@ -212,3 +212,19 @@ def test_step_rows_rejects():
     bad = cp.cpattn_posmap(8, 4, 4, 0)
     assert lib.cpattn_step_rows(ctypes.byref(good), ctypes.byref(bad), 1, ctypes.byref(rb), ctypes.byref(nk)) == -1
     assert lib.cpattn_step_rows(None, ctypes.byref(good), 1, ctypes.byref(rb), ctypes.byref(nk)) == -1
+
+
+def test_gqa_rejects_group_mismatch():
+    lib = cp.load()
+    t, l3 = _t(), _t(st=1)
+    m = cp.cpattn_posmap(64, 64, 0, 0)
+    bt, bm = ctypes.byref(t), ctypes.byref(m)
+    fwd = lambda H, H_kv: lib.cpattn_block_fwd_gqa(bt, bt, bt, 1, 1, H, H_kv, 64, 64, 64, bm, bm, 1, 0.0, None, 0, 0, 64,
+                                                   bt, ctypes.byref(l3), None)
+    assert fwd(6, 4) == -1 and "multiple" in cp.cpattn_last_error()
+    assert fwd(4, 0) == -1
+    assert fwd(2, 4) == -1
+    bwd = lambda H, H_kv: lib.cpattn_block_bwd_gqa(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1,
+                                                   H, H_kv, 64, 64, 64, bm, bm, 1, 0.0, None)
+    assert bwd(6, 4) == -1
+    assert bwd(3, -1) == -1

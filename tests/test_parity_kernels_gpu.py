@@ -10,6 +10,7 @@ import torch
 
 import context_causal_attention_cpattn_amd as cp
 from oracle import attention as oa
+from oracle import gqa as og
 from oracle import merge as om
 from oracle import rope as orope
 from oracle import shard as osh
@@ -448,3 +449,96 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
     for a_, b_ in zip(acc[:3], acc[3:]):
         assert torch.equal(a_, b_)
     assert acc[0].abs().sum() > 0
+
+
+# ----------------------------------------------------------------------------- grouped-query attention
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("H,H_kv,D", [(4, 2, 64), (6, 1, 128), (8, 4, 128), (3, 3, 64)])
+def test_block_fwd_gqa(H, H_kv, D, dtype):
+    log(f"block_fwd_gqa H={H} H_kv={H_kv} D={D} {dtype}")
+    B, Tq, Tk = 2, 200, 260
+    q, = draw_shape(B, H, Tq, D, dtype, seed=40 + H, n=1)
+    k, v = draw_shape(B, H_kv, Tk, D, dtype, seed=41 + H_kv, n=2)
+    qm, km = (200, 100, 300, 700), (260, 130, 250, 640)
+    o = torch.full((B, H, Tq, D), 7.0, device=DEV)
+    lse = torch.full((B, H, Tq), 7.0, device=DEV)
+    cp.cpattn_block_fwd_gqa(q.to(DEV), k.to(DEV), v.to(DEV), qm, km, o, lse)
+    torch.cuda.synchronize()
+    O, L = og.block_attention_fwd(f64(q), f64(k), f64(v), positions(qm), positions(km))
+    eo, el = max_err(f64(o), O), max_err(f64(lse), L)
+    log(f"  max err O {eo:.3g} LSE {el:.3g}")
+    assert eo <= tol(dtype) and el <= tol(dtype)
+
+
+@pytest.mark.parametrize("T,N,D,H,H_kv", [(512, 2, 64, 4, 2), (768, 3, 128, 4, 1), (640, 2, 128, 6, 2)])
+def test_ring_gqa_all_ranks_step_driven(T, N, D, H, H_kv):
+    """Every rank's share driven step by step (cpattn_step_rows, block forward, merge), then the
+    block backward per step; dK / dV per KV head summed over the group, against the oracle."""
+    log(f"ring gqa T={T} N={N} D={D} H={H} H_kv={H_kv}")
+    B = 1
+    q, do = draw_shape(B, H, T, D, torch.bfloat16, seed=T + H, n=2)
+    k, v = draw_shape(B, H_kv, T, D, torch.bfloat16, seed=T + H_kv + 7, n=2)
+    maps, pos = zip(*[cp.cpattn_headtail_shard(T, N, r) for r in range(N)])
+    Tl = T // N
+    kb = [gather(k, p) for p in pos]
+    vb = [gather(v, p) for p in pos]
+    dk = [torch.zeros(B, H_kv, Tl, D, device=DEV) for _ in range(N)]
+    dv = [torch.zeros(B, H_kv, Tl, D, device=DEV) for _ in range(N)]
+    gq = np.zeros((B, H, T, D))
+    O_all, L_all = og.block_attention_fwd(f64(q), f64(k), f64(v), np.arange(T), np.arange(T))
+    for r in range(N):
+        qr, dor = gather(q, pos[r]), gather(do, pos[r])
+        o = torch.empty(B, H, Tl, D, device=DEV)
+        lse = torch.empty(B, H, Tl, device=DEV)
+        ob = torch.empty_like(o)
+        lb = torch.empty_like(lse)
+        for s_ in range(N):
+            src = (r - s_) % N
+            rb, _ = cp.cpattn_step_rows(maps[r], maps[src])
+            if s_ == 0:
+                cp.cpattn_block_fwd_gqa(qr, kb[src], vb[src], maps[r], maps[src], o, lse)
+            elif rb < Tl:
+                cp.cpattn_block_fwd_gqa(qr, kb[src], vb[src], maps[r], maps[src], ob, lb, row_begin=rb)
+                cp.cpattn_lse_merge(o, lse, ob, lb, rb, Tl)
+        delta = torch.empty(B, H, Tl, device=DEV)
+        cp.cpattn_bwd_preprocess(dor, o, delta)
+        dq = torch.zeros(B, H, Tl, D, device=DEV)
+        for s_ in range(N):
+            src = (r - s_) % N
+            cp.cpattn_block_bwd_gqa(qr, kb[src], vb[src], dor, lse, delta, dq, dk[src], dv[src], maps[r], maps[src])
+        torch.cuda.synchronize()
+        rows = list(pos[r])
+        eo, el = max_err(f64(o), O_all[:, :, rows]), max_err(f64(lse), L_all[:, :, rows])
+        log(f"  rank {r} forward: O {eo:.3g} LSE {el:.3g}")
+        assert eo <= TOL_BF16 and el <= TOL_BF16
+        gq[:, :, rows] = f64(dq)
+    gk, gv = np.zeros((B, H_kv, T, D)), np.zeros((B, H_kv, T, D))
+    for i in range(N):
+        gk[:, :, list(pos[i])] = f64(dk[i])
+        gv[:, :, list(pos[i])] = f64(dv[i])
+    dQ, dK, dV, _, _ = og.causal_attention_bwd(f64(q), f64(k), f64(v), f64(do))
+    e = (max_err(gq, dQ), max_err(gk, dK), max_err(gv, dV))
+    log(f"  backward: dq {e[0]:.3g} dk {e[1]:.3g} dv {e[2]:.3g}")
+    assert max(e) <= TOL_BF16
+
+
+def test_gqa_with_group_one_is_bitwise_mha():
+    """H_kv = H takes the same path as the plain entry points: identical bits."""
+    B, H, T, D = 1, 3, 300, 64
+    q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=5, n=4)
+    m = (T, T // 2, 0, T)
+    q, k, v, do = (x.to(DEV) for x in (q, k, v, do))
+    o1, l1, o2, l2 = (torch.empty(B, H, T, D, device=DEV), torch.empty(B, H, T, device=DEV),
+                      torch.empty(B, H, T, D, device=DEV), torch.empty(B, H, T, device=DEV))
+    cp.cpattn_block_fwd(q, k, v, m, m, o1, l1)
+    cp.cpattn_block_fwd_gqa(q, k, v, m, m, o2, l2)
+    delta = torch.empty(B, H, T, device=DEV)
+    cp.cpattn_bwd_preprocess(do, o1, delta)
+    g1 = [torch.zeros(B, H, T, D, device=DEV) for _ in range(3)]
+    g2 = [torch.zeros(B, H, T, D, device=DEV) for _ in range(3)]
+    cp.cpattn_block_bwd(q, k, v, do, l1, delta, *g1, m, m)
+    cp.cpattn_block_bwd_gqa(q, k, v, do, l1, delta, *g2, m, m)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
