@@ -104,8 +104,8 @@ class Share:
         self.l_blk = torch.empty(w.B, w.H, Tl, **f32)
         self.delta = torch.empty(w.B, w.H, Tl, **f32)
         self.dq = torch.zeros(w.B, w.H, Tl, w.D, **f32)
-        self.dk = [torch.zeros(w.B, w.H, Tl, w.D, **f32) for _ in range(N)]
-        self.dv = [torch.zeros(w.B, w.H, Tl, w.D, **f32) for _ in range(N)]
+        self.dk = [torch.zeros(w.B, w.kv_heads, Tl, w.D, **f32) for _ in range(N)]
+        self.dv = [torch.zeros(w.B, w.kv_heads, Tl, w.D, **f32) for _ in range(N)]
         # per ring step: (src, row_begin, visible pairs per (b, h))
         self.steps = []
         qp = self.pos[0]
@@ -132,6 +132,8 @@ class Share:
         st = cp._stream(None)
         bf16 = cp._dtype(self.q)
         B, H, Tl, D, Tk = w.B, w.H, w.local_len, w.D, w.local_len
+        Hkv = w.kv_heads
+        gqa = Hkv != H  # grouped-query attention: the _gqa entry points
         q, do = T(self.q), T(self.do)
         o, lse, ob, lb = T(self.o), T(self.lse, 3), T(self.o_blk), T(self.l_blk, 3)
         delta, dq = T(self.delta, 3), T(self.dq)
@@ -158,9 +160,14 @@ class Share:
                              (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
                 k = kr
             oo, ll = (o, lse) if s == 0 else (ob, lb)
-            plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd,
-                         (by(qf), by(k), by(v), bf16, B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, None, 0,
-                          0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
+            if gqa:
+                plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_gqa,
+                             (by(qf), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, None, 0,
+                              0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
+            else:
+                plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd,
+                             (by(qf), by(k), by(v), bf16, B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, None, 0,
+                              0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
             if s > 0:
                 plan.append(("lse_merge", (Tl - rb) * self.bh * (12 * D + 12), lib.cpattn_lse_merge,
                              (by(o), by(lse), by(ob), by(lb), B, H, Tl, D, rb, Tl, st)))
@@ -178,6 +185,11 @@ class Share:
                     plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
                                  (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
                     k, q = kr, qf
+                if gqa:
+                    plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd_gqa,
+                                 (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
+                                  B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, st)))
+                    continue
                 if not split_bwd:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
@@ -534,7 +546,7 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for name in ("win16k", "win32k"):
+        for name in ("win16k", "win32k", "gqa16k"):
             wx = BY_NAME[name]
             sx = Share(wx, seed_do=wx.seed + 1000)
             sx.split_bwd = True  # at D = 128 the two halves are separate launches anyway
@@ -543,7 +555,8 @@ def main():
             fl = sx.flops(bwd)
             extra[name] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
                            "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
-                           "parts": "forward + backward" + (" with rotary" if wx.rope_theta else ""),
+                           "parts": "forward + backward" + (" with rotary" if wx.rope_theta else "") +
+                                    (f" (grouped-query, {wx.kv_heads} KV heads)" if wx.kv_heads != wx.H else ""),
                            "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
                                            "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
             del sx

@@ -11,6 +11,8 @@ Workloads (global token order, all inputs i.i.d. N(0, 1)):
   win16k    B=1 H=32 D=128 T=16384 ring degree 2, bf16 inputs
   win32k    B=1 H=16 D=128 T=32768 ring degree 2, bf16 inputs, rotary theta 10000
   bwd16k    B=1 H=32 D=128 T=16384 ring degree 2, bf16 inputs, upstream dO drawn too
+  gqa16k    the 16k window with 8 KV heads shared by groups of 4 query heads
+            (grouped-query attention, the next row after the hot path), dO drawn
 
 Seeds are 1234 + k for the k-th workload in that order; 1234 is the init seed
 used throughout the BluScriptCP development log (entry of 2026-06-05 on the
@@ -40,6 +42,11 @@ class Workload:
     rope_theta: float = 0.0
     backward: bool = False
     note: str = ""
+    H_kv: int = 0  # KV heads (0: one per query head)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def seed(self) -> int:
@@ -71,6 +78,8 @@ WORKLOADS = [
              note="32k window with rotary at global positions; one head share of 32"),
     Workload("bwd16k", 4, B=1, H=32, D=128, T=16384, ring=2, dtype="bf16", backward=True,
              note="16k window forward + backward; all ranks' shares"),
+    Workload("gqa16k", 5, B=1, H=32, D=128, T=16384, ring=2, dtype="bf16", backward=True, H_kv=8,
+             note="16k window, grouped-query attention with 8 KV heads (groups of 4)"),
 ]
 
 BY_NAME = {w.name: w for w in WORKLOADS}
@@ -81,15 +90,16 @@ def draw(w: Workload, heads: slice | None = None, seed: int | None = None):
 
     The tensors are drawn in fp32 from ``torch.Generator`` seeded with
     ``w.seed`` (or ``seed``) in the order q, k, v, do, then rounded to the
-    workload dtype. ``heads`` selects a head range after drawing, so a subset
-    has exactly the values of the full draw.
+    workload dtype; k and v have ``w.kv_heads`` heads. ``heads`` selects a
+    head range after drawing, so a subset has exactly the values of the full
+    draw.
     """
     g = torch.Generator(device="cpu")
     g.manual_seed(w.seed if seed is None else seed)
-    shape = (w.B, w.H, w.T, w.D)
     names = ["q", "k", "v"] + (["do"] if w.backward else [])
     out = {}
     for n in names:
+        shape = (w.B, w.kv_heads if n in ("k", "v") else w.H, w.T, w.D)
         t = torch.randn(shape, dtype=torch.float32, generator=g)
         t = t.to(w.torch_dtype)
         if heads is not None:
