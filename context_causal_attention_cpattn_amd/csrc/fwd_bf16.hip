@@ -79,23 +79,36 @@ __device__ __forceinline__ void wait_units(int units) {
 // so that the matrix cores and the vector ALUs of one wave work at the same time.
 // LDS holds NS K tiles and NS V tiles. Load group g = {V_g, K_{g+1}} is issued
 // (in that order) at the top of iteration g - NS + 1 and consumed in iteration g.
-template <int D, int NS>
+//
+// KS = 2 splits the keys of a workgroup between two pairs of waves, for ring
+// steps too small to fill the device: waves 0 and 1 own 32 query rows each and
+// take the even key tiles, waves 2 and 3 own the same rows and take the odd
+// tiles, each pair with its own LDS rings; at the end the odd pair's partial
+// results (accumulator, reference max, row sum) are merged into the even pair's
+// through LDS. A workgroup then covers 64 rows, so a step has twice as many
+// workgroups, each walking half the keys.
+template <int D, int NS, int KS>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) char ksm[NS][C::TILEB];
-  __shared__ __attribute__((aligned(1024))) char vsm[NS][C::TILEB];
+  static_assert(KS == 1 || (KS == 2 && D == 64), "key split: 64-wide heads only");
+  constexpr int NR = kNW / KS;     // waves per key share (one 32-row block each)
+  constexpr int ROWS = 32 * NR;    // query rows per workgroup
+  __shared__ __attribute__((aligned(1024))) char ksm[KS][NS][C::TILEB];
+  __shared__ __attribute__((aligned(1024))) char vsm[KS][NS][C::TILEB];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
+  const int rb = w % NR;  // row block of this wave
+  const int kh = w / NR;  // key share of this wave: tiles kh, kh + KS, kh + 2 KS, ...
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = L / n_qt;
   const int qt = n_qt - 1 - (L - bh * n_qt);
   const int b = bh / a.H, hh = bh - b * a.H;
-  const int q0 = a.row_begin + qt * kBM;
-  const int row = q0 + 32 * w + lq;
+  const int q0 = a.row_begin + qt * ROWS;
+  const int row = q0 + 32 * rb + lq;
   const bool row_ok = row < a.row_end;
 
   const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh;
@@ -119,21 +132,26 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]));
 
   // ---- key range of this workgroup
-  const int last_row = (q0 + kBM < a.row_end ? q0 + kBM : a.row_end) - 1;
+  const int last_row = (q0 + ROWS < a.row_end ? q0 + ROWS : a.row_end) - 1;
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
-  const int n_kt = (n_vis + kBN - 1) / kBN;
+  const int n_kt = (n_vis + kBN - 1) / kBN;   // key tiles of the workgroup
+  const int n_jmax = (n_kt + KS - 1) / KS;     // tiles of the larger share
+  const int n_j = n_kt > kh ? (n_kt - kh + KS - 1) / KS : 0;  // tiles of this wave's share
+  auto tile = [&](int j) { return KS * j + kh; };
   // Positions increase with the local index, so the keys a query sees are the prefix
   // [0, lim) of the block; the wave's first row has the smallest limit.
-  const int wave_first = q0 + 32 * w < a.row_end ? q0 + 32 * w : a.row_end - 1;
+  const int wave_first = q0 + 32 * rb < a.row_end ? q0 + 32 * rb : a.row_end - 1;
   const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
 
-  // ---- direct global -> LDS loads: wave w fills the 1 KB slots w + kNW*i (i < NI) of each
-  // tile. Slot position p = 64*slot + lane is tile row p / CPR, physical chunk p % CPR. The
-  // rows of a lane's NI slots differ by 64*kNW/CPR, a multiple of the swizzle period, so the
-  // lane's byte offset is the same for all of them and only the (scalar) row base moves.
-  constexpr int kSlotRows = 64 * kNW / C::CPR;  // rows between a lane's consecutive slots
-  const int ld_r0 = (64 * w + l) / C::CPR;
+  // ---- direct global -> LDS loads: the NR waves of a key share fill the 1 KB slots of that
+  // share's tiles, wave rb the slots rb + NR*i (i < NIH). Slot position p = 64*slot + lane is
+  // tile row p / CPR, physical chunk p % CPR. The rows of a lane's slots differ by
+  // 64*NR/CPR, a multiple of the swizzle period, so the lane's byte offset is the same for
+  // all of them and only the (scalar) row base moves.
+  constexpr int NIH = C::NI * KS;                // loads per wave per tile
+  constexpr int kSlotRows = 64 * NR / C::CPR;  // rows between a lane's consecutive slots
+  const int ld_r0 = (64 * rb + l) / C::CPR;
   const int ld_col = ((l % C::CPR) ^ C::mask(ld_r0)) * 8;
   const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
   const unsigned vo = (unsigned)((ld_r0 * a.v.st + ld_col) * 2);
@@ -143,21 +161,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     const char* tb = (const char*)(base + (int64_t)kt * kBN * st);
     if (kt * kBN + kBN <= a.Tk) {
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i)
-        load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (w + kNW * i) * 1024);
+      for (int i = 0; i < NIH; ++i)
+        load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (rb + NR * i) * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < C::NI; ++i) {
+      for (int i = 0; i < NIH; ++i) {
         const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - kt * kBN);
-        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (w + kNW * i) * 1024);
+        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (rb + NR * i) * 1024);
       }
     }
   };
-  auto issue_group = [&](int g) {
-    if (g < n_kt) issue(vp, a.v.st, vo, g, vsm[g % NS]);
-    if (g + 1 < n_kt) issue(kp, a.k.st, ko, g + 1, ksm[(g + 1) % NS]);
+  // load group j of this share: V of its tile j, then K of its tile j+1
+  auto issue_group = [&](int j) {
+    if (j < n_j) issue(vp, a.v.st, vo, tile(j), vsm[kh][j % NS]);
+    if (j + 1 < n_j) issue(kp, a.k.st, ko, tile(j + 1), ksm[kh][(j + 1) % NS]);
   };
-  auto group_units = [&](int g) { return (g < n_kt ? 1 : 0) + (g + 1 < n_kt ? 1 : 0); };
+  auto group_units = [&](int j) { return (j < n_j ? 1 : 0) + (j + 1 < n_j ? 1 : 0); };
 
   // ---- per-lane LDS byte offsets (swizzled)
   // K operand: row 32kb + lq, logical chunk 2c + h
@@ -209,9 +228,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     return 32 * kb + 8 * (r >> 2) + (r & 3) < rel ? v : -INFINITY;
   };
 
-  // ---- prologue: K_0, groups 0 .. NS-2, then S_0 and its row max
-  if (n_kt > 0) issue(kp, a.k.st, ko, 0, ksm[0]);
-  int pending = 0;  // load units issued after K_0
+  // ---- prologue: K of the share's tile 0, groups 0 .. NS-2, then S and its row max. Every
+  // wave of the workgroup passes the same number of barriers: one here when the workgroup
+  // has any tile, one per tile of the larger share (a share with fewer tiles pads).
+  if (n_j > 0) issue(kp, a.k.st, ko, tile(0), ksm[kh][0]);
+  int pending = 0;  // load units issued after that K tile
 #pragma unroll
   for (int g = 0; g < NS - 1; ++g) {
     issue_group(g);
@@ -220,12 +241,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   f32x16 sA[2] = {f32x16{}, f32x16{}}, sB[2];
   float mx = -INFINITY;
   if (n_kt > 0) {
-    wait_units<C::NI>(pending);
+    wait_units<NIH>(pending);
     __syncthreads();
-    sA[0] = scores(ksm[0], 0);
-    sA[1] = scores(ksm[0], 1);
-    if (needs_mask(0)) {
-      const int rel = mask_rel(0);
+  }
+  if (n_j > 0) {
+    sA[0] = scores(ksm[kh][0], 0);
+    sA[1] = scores(ksm[kh][0], 1);
+    if (needs_mask(tile(0))) {
+      const int rel = mask_rel(tile(0));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -239,19 +262,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     mx = fmaxf(m, __shfl_xor(m, 32));
   }
 
-  // One key tile. `sc` holds S_kt (masked) and `mx` its row max on entry; with
-  // NEXT, S_kt+1 is formed into `sn` (masked) and `mx` becomes its max.
+  // Tile j of this wave's share. `sc` holds its S (masked) and `mx` its row max on entry;
+  // with NEXT, S of tile j+1 is formed into `sn` (masked) and `mx` becomes its max.
   // The interleaving is fixed by scheduling fences: each MFMA is followed by the
   // slice of vector work that runs while it executes.
-  auto step = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2], auto next_tag) __attribute__((always_inline)) {
+  auto step = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], auto next_tag) __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
-    // group kt (V_kt, K_kt+1) has landed once only groups kt+1 .. kt+NS-2 are outstanding
+    // group j (V_j, K_j+1) has landed once only groups j+1 .. j+NS-2 are outstanding
     int later = 0;
 #pragma unroll
-    for (int g = 1; g <= NS - 2; ++g) later += group_units(kt + g);
-    wait_units<C::NI>(later);
-    __syncthreads();  // group kt visible to all waves; all waves are done with V_kt-1 and K_kt
-    issue_group(kt + NS - 1);
+    for (int g = 1; g <= NS - 2; ++g) later += group_units(j + g);
+    wait_units<NIH>(later);
+    __syncthreads();  // group j visible to its share; every wave is done with V_j-1 and K_j
+    issue_group(j + NS - 1);
 
     // ---- lazy rescale: the running max moves only when a score exceeds it by 2^8
     const float m_tile = mx * sl2;
@@ -272,13 +295,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     // matrix cores form S_kt+1 = K_kt+1 Q^T. The 2*NC K operands are read LA MFMAs ahead.
     constexpr int EA = 16 / C::NC;  // score elements per MFMA slot
     constexpr int LA = 4;
-    const char* kn = ksm[(kt + 1) % NS];
-    auto kread = [&](int j) { return *(const bf16x8*)(kn + 32 * (j / C::NC) * C::ROWB + koff[j % C::NC]); };
+    const char* kn = ksm[kh][(j + 1) % NS];
+    auto kread = [&](int jj) { return *(const bf16x8*)(kn + 32 * (jj / C::NC) * C::ROWB + koff[jj % C::NC]); };
     bf16x8 pb[4];
     bf16x8 ka[LA];
     if constexpr (NEXT) {
 #pragma unroll
-      for (int j = 0; j < LA; ++j) ka[j] = kread(j);
+      for (int jj = 0; jj < LA; ++jj) ka[jj] = kread(jj);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -286,9 +309,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
 #pragma unroll
       for (int c = 0; c < C::NC; ++c) {
         if constexpr (NEXT) {
-          const int j = C::NC * kb + c;
-          acc_s = mfma32(ka[j % LA], qf[c], acc_s);
-          if (j + LA < 2 * C::NC) ka[j % LA] = kread(j + LA);
+          const int jj = C::NC * kb + c;
+          acc_s = mfma32(ka[jj % LA], qf[c], acc_s);
+          if (jj + LA < 2 * C::NC) ka[jj % LA] = kread(jj + LA);
         }
 #pragma unroll
         for (int e = 0; e < EA; ++e) {
@@ -305,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     // ---- phase B: O^T += V^T P^T (V^T rows = d, 8 keys 16t + 4h + {0..3}, +8), while the
     // vector ALUs take the row max of S_kt+1. V^T operands are read one MFMA ahead.
     constexpr int EB = 32 / (4 * C::NDB);  // score elements per MFMA slot
-    const char* vs = vsm[kt % NS];
+    const char* vs = vsm[kh][j % NS];
     bf16x8 va[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -335,8 +358,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     if constexpr (NEXT) {
       // a tile that reaches past the wave's smallest limit is masked and its max redone
       asm volatile("" : "+v"(m2));  // keep the unmasked max beside the PV products
-      if (needs_mask(kt + 1)) {
-        const int rel = mask_rel(kt + 1);
+      if (needs_mask(tile(j + 1))) {
+        const int rel = mask_rel(tile(j + 1));
         m2 = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -352,20 +375,50 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
 
   using T_ = std::integral_constant<bool, true>;
   using F_ = std::integral_constant<bool, false>;
-  auto run = [&](int kt, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
-    step(kt, sc, sn, T_{});
+  auto run = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) __attribute__((always_inline)) {
+    step(j, sc, sn, T_{});
   };
   // two tiles per trip so that the score registers alternate instead of being copied
-  int kt = 0;
-  for (; kt + 2 < n_kt; kt += 2) {
-    run(kt, sA, sB);
-    run(kt + 1, sB, sA);
+  int j = 0;
+  for (; j + 2 < n_j; j += 2) {
+    run(j, sA, sB);
+    run(j + 1, sB, sA);
   }
-  if (kt + 1 < n_kt) {
-    run(kt, sA, sB);
-    step(kt + 1, sB, sA, F_{});
-  } else if (kt < n_kt) {
-    step(kt, sA, sB, F_{});
+  if (j + 1 < n_j) {
+    run(j, sA, sB);
+    step(j + 1, sB, sA, F_{});
+  } else if (j < n_j) {
+    step(j, sA, sB, F_{});
+  }
+  for (int e = n_j; e < n_jmax; ++e) __syncthreads();  // a share with fewer tiles pads
+
+  if constexpr (KS == 2) {
+    // ---- merge the odd share's partial result into the even share's, rows alike:
+    // [NR waves][NDB*16 accumulator values, reference max, row-sum partial][64 lanes]
+    constexpr int NV = C::NDB * 16 + 2;
+    static_assert(NR * NV * 64 * 4 <= KS * NS * C::TILEB, "merge staging fits the K rings");
+    float* cb = (float*)&ksm[0][0][0] + rb * NV * 64;
+    __syncthreads();  // every wave is done with its rings
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[(16 * db + r) * 64 + l] = acc[db][r];
+      cb[(NV - 2) * 64 + l] = m_run;
+      cb[(NV - 1) * 64 + l] = l_part;
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    const float m1 = cb[(NV - 2) * 64 + l], l1 = cb[(NV - 1) * 64 + l];
+    const float mm = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * a0 + cb[(16 * db + r) * 64 + l] * a1;
+    l_part = l_part * a0 + l1 * a1;
+    m_run = mm;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
@@ -393,11 +446,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
 template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
-  const int n_qt = (rows + kBM - 1) / kBM;
-  const int64_t grid = (int64_t)n_qt * a.B * a.H;
-  if (grid <= 0) return hipSuccess;
+  const int64_t bh = (int64_t)a.B * a.H;
+  const int64_t grid1 = (int64_t)((rows + kBM - 1) / kBM) * bh;
+  if (grid1 <= 0) return hipSuccess;
+  if constexpr (D == 64) {
+    // fewer than two workgroups per CU: split each workgroup's keys between two wave pairs
+    if (grid1 < 512) {
+      const int n_qt = (rows + kBM / 2 - 1) / (kBM / 2);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s, a, n_qt);
+      return hipGetLastError();
+    }
+  }
   constexpr int NS = D == 64 ? 4 : 2;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NS>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
+  const int n_qt = (rows + kBM - 1) / kBM;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NS, 1>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
