@@ -289,10 +289,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 constexpr int kQPerWG = 32 * kNW;  // 128 query rows per workgroup
 constexpr int kKB = 32;            // keys per dQ tile: one 32-key MFMA block
 
-template <int D, int NS>
+template <int D, int NS, int KS>
 struct DqLds {
-  alignas(1024) char sk[NS][kKB * BCfg<D>::ROWB];
-  alignas(1024) char sv[NS][kKB * BCfg<D>::ROWB];
+  alignas(1024) char sk[KS][NS][kKB * BCfg<D>::ROWB];
+  alignas(1024) char sv[KS][NS][kKB * BCfg<D>::ROWB];
 };
 
 // Workgroup Lg of the dQ grid (Lg = bh * n_qt + heavy-first query tile).
@@ -302,31 +302,42 @@ struct DqLds {
 //            (at D = 128 followed by dP_u+1^T, which keeps phase A within the registers of
 //            two waves per SIMD)
 // so tiles u and u+1 are read in iteration u, and the LDS ring holds NS >= 3 tiles.
-template <int D, int NS>
-__device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLds<D, NS>& sm) {
+// KS = 2 splits the key tiles of a workgroup between two pairs of waves that own the
+// same 64 rows (even tiles to waves 0-1, odd tiles to waves 2-3, each pair with its own
+// rings); the odd pair's dQ partial is added to the even pair's through LDS at the end.
+template <int D, int NS, int KS>
+__device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLds<D, NS, KS>& sm) {
   using C = BCfg<D>;
   static_assert(NS >= 3 && NS <= 5, "pipeline depth");
-  constexpr int NIQ = kKB * C::CPR / (64 * kNW);  // direct loads per wave per tile (K or V)
-  constexpr int kSlotRows = 64 * kNW / C::CPR;    // rows between a lane's consecutive slots
+  static_assert(KS == 1 || (KS == 2 && D == 64), "key split: 64-wide heads only");
+  constexpr int NR = kNW / KS;                        // waves per key share
+  constexpr int ROWS = 32 * NR;                       // query rows per workgroup
+  constexpr int NIQ = kKB * C::CPR / (64 * NR);       // direct loads per wave per tile (K or V)
+  constexpr int kSlotRows = 64 * NR / C::CPR;         // rows between a lane's consecutive slots
   static_assert(NIQ >= 1 && kSlotRows % 16 == 0, "tile layout");
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
+  const int rb = w % NR;  // row block of this wave
+  const int kh = w / NR;  // key share: tiles kh, kh + KS, ...
   const int bh = Lg / n_qt;
   const int qt = n_qt - 1 - (Lg - bh * n_qt);
   const int b = bh / a.H, hh = bh - b * a.H;
-  const int q0 = qt * kQPerWG;
-  const int row = q0 + 32 * w + lq;
+  const int q0 = qt * ROWS;
+  const int row = q0 + 32 * rb + lq;
   const bool row_ok = row < a.Tq;
 
   // ---- key range: the keys row r sees are the prefix [0, lim) of the block
   const int qpos = a.qm.pos(row_ok ? row : a.Tq - 1);
-  const int last_row = (q0 + kQPerWG < a.Tq ? q0 + kQPerWG : a.Tq) - 1;
+  const int last_row = (q0 + ROWS < a.Tq ? q0 + ROWS : a.Tq) - 1;
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
   const int n_kt = (n_vis + kKB - 1) / kKB;
   if (n_kt == 0) return;  // no key of this block is visible to these rows: nothing to add
-  const int wave_first = q0 + 32 * w < a.Tq ? q0 + 32 * w : a.Tq - 1;
+  const int n_jmax = (n_kt + KS - 1) / KS;                    // tiles of the larger share
+  const int n_j = n_kt > kh ? (n_kt - kh + KS - 1) / KS : 0;  // tiles of this wave's share
+  auto tile = [&](int j) { return KS * j + kh; };
+  const int wave_first = q0 + 32 * rb < a.Tq ? q0 + 32 * rb : a.Tq - 1;
   const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
   const float sl2 = a.scale * kLog2e;
@@ -358,9 +369,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]), "v"(df[c]));
   asm volatile("" ::"v"(lse2), "v"(dl));
 
-  // ---- direct global -> LDS loads: wave w fills 1 KB slots w + kNW*i of each tile; the
-  // rows of a lane's slots differ by a multiple of the swizzle period (one lane offset)
-  const int ld_r0 = (64 * w + l) / C::CPR;
+  // ---- direct global -> LDS loads: wave rb of a share fills 1 KB slots rb + NR*i of that
+  // share's tiles; the rows of a lane's slots differ by a multiple of the swizzle period
+  // (one lane offset)
+  const int ld_r0 = (64 * rb + l) / C::CPR;
   const int ld_col = ((l % C::CPR) ^ swz_mask<D>(ld_r0)) * 8;
   const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
   const unsigned vo = (unsigned)((ld_r0 * a.v.st + ld_col) * 2);
@@ -368,18 +380,19 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
     const char* tb = (const char*)(base + (int64_t)kt * kKB * st);
     if (kt * kKB + kKB <= a.Tk) {
 #pragma unroll
-      for (int i = 0; i < NIQ; ++i) load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (w + kNW * i) * 1024);
+      for (int i = 0; i < NIQ; ++i) load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (rb + NR * i) * 1024);
     } else {  // rows past the block repeat the last key (masked)
 #pragma unroll
       for (int i = 0; i < NIQ; ++i) {
         const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - kt * kKB);
-        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (w + kNW * i) * 1024);
+        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (rb + NR * i) * 1024);
       }
     }
   };
-  auto issue_tile = [&](int kt) {
-    issue(kp, a.k.st, ko, kt, sm.sk[kt % NS]);
-    issue(vp, a.v.st, vo, kt, sm.sv[kt % NS]);
+  // tile j of this wave's share
+  auto issue_tile = [&](int j) {
+    issue(kp, a.k.st, ko, tile(j), sm.sk[kh][j % NS]);
+    issue(vp, a.v.st, vo, tile(j), sm.sv[kh][j % NS]);
   };
 
   const Offs<D> off(l);
@@ -395,36 +408,41 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
     for (int r = 0; r < 16; ++r) sv[r] = 8 * (r >> 2) + (r & 3) < rel ? sv[r] : -INFINITY;
   };
 
-  // ---- prologue: tiles 0 .. NS-2 in flight, then S_0 and dP_0
+  // ---- prologue: the share's tiles 0 .. NS-2 in flight, then S and dP of its tile 0. Every
+  // wave passes one barrier here and one per tile of the larger share (a share with fewer
+  // tiles pads).
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < n_kt) issue_tile(j);
-  wait_tiles<2 * NIQ>(min(NS - 2, n_kt - 1));
+    if (j < n_j) issue_tile(j);
+  wait_tiles<2 * NIQ>(min(NS - 2, n_j - 1));
   __syncthreads();
   f32x16 sA = f32x16{}, dA = f32x16{}, sB, dB;
+  if (n_j > 0) {
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    sA = mfma32(*(const bf16x8*)(sm.sk[0] + off.ro[c]), qf[c], sA);
-    dA = mfma32(*(const bf16x8*)(sm.sv[0] + off.ro[c]), df[c], dA);
+    for (int c = 0; c < C::NC; ++c) {
+      sA = mfma32(*(const bf16x8*)(sm.sk[kh][0] + off.ro[c]), qf[c], sA);
+      dA = mfma32(*(const bf16x8*)(sm.sv[kh][0] + off.ro[c]), df[c], dA);
+    }
+    if (needs_mask(tile(0))) apply_mask(sA, tile(0));
   }
-  if (needs_mask(0)) apply_mask(sA, 0);
 
-  // One tile u: `s`, `dp` hold S_u^T (masked) and dP_u^T; with NEXT, S_u+1 and dP_u+1 are
-  // formed into `sn`, `dpn`. Scheduling fences pin the MFMA / vector interleave.
+  // Tile u of this wave's share: `s`, `dp` hold its S^T (masked) and dP^T; with NEXT, those
+  // of tile u+1 are formed into `sn`, `dpn`. Scheduling fences pin the MFMA / vector
+  // interleave.
   auto step = [&](int u, f32x16& s, f32x16& dp, f32x16& sn, f32x16& dpn, auto next_tag)
                   __attribute__((always_inline)) {
     constexpr bool NEXT = decltype(next_tag)::value;
-    if constexpr (NEXT) wait_tiles<2 * NIQ>(min(NS - 3, n_kt - 2 - u));  // tile u+1 has landed
+    if constexpr (NEXT) wait_tiles<2 * NIQ>(min(NS - 3, n_j - 2 - u));  // tile u+1 has landed
     __syncthreads();  // tile u+1 visible; every wave is done with tile u-1
-    if (u + NS - 1 < n_kt) issue_tile(u + NS - 1);
+    if (u + NS - 1 < n_j) issue_tile(u + NS - 1);
 
     // ---- phase A: dS_u = P_u (dP_u - delta) in bf16, with S_u+1 (and dP_u+1) on the matrix cores
     constexpr bool DP_IN_A = D == 64;
     constexpr int NM = (DP_IN_A ? 2 : 1) * C::NC;  // MFMAs of phase A (S and dP chains interleaved)
     constexpr int EA = 16 / NM > 0 ? 16 / NM : 1;
     constexpr int LA = D == 64 ? 4 : 2;  // operand reads in flight ahead of their MFMA
-    const char* kn = sm.sk[(u + 1) % NS];
-    const char* vn = sm.sv[(u + 1) % NS];
+    const char* kn = sm.sk[kh][(u + 1) % NS];
+    const char* vn = sm.sv[kh][(u + 1) % NS];
     // operand j of phase A: K row chunk j (S only) or K / V row chunk j/2 (S and dP)
     auto rd = [&](int j) {
       if constexpr (DP_IN_A) return *(const bf16x8*)(((j & 1) ? vn : kn) + off.ro[j >> 1]);
@@ -461,7 +479,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
     }
 
     // ---- phase B: dQ^T += K^T dS^T ; K^T operand rows = d, 8 keys 16t + 4h + {0..3}, +8
-    const char* K = sm.sk[u % NS];
+    const char* K = sm.sk[kh][u % NS];
     bf16x8 kt8[C::NDB];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
@@ -488,7 +506,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
       }
     }
     if constexpr (NEXT)
-      if (needs_mask(u + 1)) apply_mask(sn, u + 1);
+      if (needs_mask(tile(u + 1))) apply_mask(sn, tile(u + 1));
   };
 
   using T_ = std::integral_constant<bool, true>;
@@ -496,11 +514,32 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   // last tile also forms the scores of a tile past the end from a stale (in-bounds) LDS
   // stage; they are never used, and one code path keeps the loop within the registers.
   int u = 0;
-  for (; u + 1 < n_kt; u += 2) {
+  for (; u + 1 < n_j; u += 2) {
     step(u, sA, dA, sB, dB, T_{});
     step(u + 1, sB, dB, sA, dA, T_{});
   }
-  if (u < n_kt) step(u, sA, dA, sB, dB, T_{});
+  if (u < n_j) step(u, sA, dA, sB, dB, T_{});
+  for (int e = n_j; e < n_jmax; ++e) __syncthreads();  // a share with fewer tiles pads
+
+  if constexpr (KS == 2) {
+    // ---- add the odd share's dQ^T partial to the even share's (same rows, same layout)
+    constexpr int NV = C::NDB * 16;
+    static_assert(NR * NV * 64 * 4 <= KS * NS * kKB * C::ROWB, "staging fits the K rings");
+    float* cb = (float*)&sm.sk[0][0][0] + rb * NV * 64;
+    __syncthreads();  // every wave is done with its rings
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cb[(16 * db + r) * 64 + l] = acc[db][r];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] += cb[(16 * db + r) * 64 + l];
+  }
 
   if (row_ok) {
     float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
@@ -523,10 +562,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
-template <int D, int NS>
+template <int D, int NS, int KS>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
-  __shared__ DqLds<D, NS> sm;
-  dq_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
+  __shared__ DqLds<D, NS, KS> sm;
+  dq_body<D, NS, KS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
 }
 
 // Both halves of the block backward in one grid: the first n_dq workgroups (a
@@ -535,16 +574,16 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
 // each alone is too small to. Workgroups are dealt to the 8 XCDs round-robin by
 // id, so both roles land on every XCD; within a role the ids are remapped as in
 // the single-role kernels.
-template <int D, int NSK, int NSQ>
+template <int D, int NSK, int NSQ, int KSQ>
 __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_dq, int n_dq_pad) {
   __shared__ union {
     DkdvLds<D, NSK> kv;
-    DqLds<D, NSQ> q;
+    DqLds<D, NSQ, KSQ> q;
   } sm;
   const int id = blockIdx.x;
   if (id < n_dq_pad) {
     const int L = xcd_remap(id, n_dq_pad);
-    if (L < n_dq) dq_body<D, NSQ>(a, L, n_qt, sm.q);
+    if (L < n_dq) dq_body<D, NSQ, KSQ>(a, L, n_qt, sm.q);
   } else {
     dkdv_body<D, NSK>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
   }
@@ -558,13 +597,21 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;           // (b, query head) for dQ
   const int64_t bkv = (int64_t)a.B * (a.H / a.G);  // (b, KV head) for dK / dV
+  // fewer than two dQ workgroups per CU: split their keys between two wave pairs
+  const bool split = D == 64 && bh * n_qt < 512;
+  const int n_qt2 = (a.Tq + kQPerWG / 2 - 1) / (kQPerWG / 2);
   if constexpr (D == 64) {
     // both kernels keep two workgroups per CU at this width, so one grid costs nothing
     if (which == 3) {
-      const int64_t n_dq = bh * n_qt, n_dq_pad = (n_dq + 7) / 8 * 8;
+      const int nq = split ? n_qt2 : n_qt;
+      const int64_t n_dq = bh * nq, n_dq_pad = (n_dq + 7) / 8 * 8;
       const int64_t grid = n_dq_pad + bkv * n_kt;
-      hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
-                         n_qt, (int)n_dq, (int)n_dq_pad);
+      if (split)
+        hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 2>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
+                           nq, (int)n_dq, (int)n_dq_pad);
+      else
+        hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 1>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
+                           nq, (int)n_dq, (int)n_dq_pad);
       return hipGetLastError();
     }
   }
@@ -574,7 +621,13 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (which & 2) {
-    hipLaunchKernelGGL((dq_kernel<D, NSQ>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
+    if constexpr (D == 64) {
+      if (split) {
+        hipLaunchKernelGGL((dq_kernel<D, NSQ, 2>), dim3((unsigned)(bh * n_qt2)), dim3(64 * kNW), 0, s, a, n_qt2);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((dq_kernel<D, NSQ, 1>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
     return hipGetLastError();
   }
   return hipSuccess;
