@@ -82,8 +82,12 @@ struct DkdvLds {
 };
 
 // Workgroup Lg of the dK/dV grid (Lg = bh * n_kt + key tile).
-template <int D, int NS>
+// PART selects what one launch forms: 0 both dK and dV, 1 dV only (no V rows, no dP),
+// 2 dK only. A launch of one part keeps one accumulator, which brings the 128-wide
+// kernel within two waves per SIMD at the price of forming S in both launches.
+template <int D, int NS, int PART>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, DkdvLds<D, NS>& sm) {
+  constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using C = BCfg<D>;
   auto& sq = sm.sq;
   auto& sdo = sm.sdo;
@@ -111,12 +115,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     for (int c = 0; c < C::NC; ++c) {
       u32x4 z = {0u, 0u, 0u, 0u};
       kf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(kk + 16 * c + 8 * h) : z);
-      vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
+      if constexpr (WANT_DK) vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
     }
   }
   // complete the register loads before the tile loop (see the forward kernel)
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
+  for (int c = 0; c < C::NC; ++c) {
+    asm volatile("" ::"v"(kf[c]));
+    if constexpr (WANT_DK) asm volatile("" ::"v"(vf[c]));
+  }
   // Positions increase with the local index, so the query rows that see this lane's key
   // are [qlo, Tq); the wave's last key has the largest qlo.
   const int qlo = a.causal ? a.qm.count_lt(a.km.pos(key_ok ? key : a.Tk - 1)) : 0;
@@ -202,25 +209,42 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       // operands of S = Q K^T and dP = dO V^T for 32 query rows, read as one batch
-      bf16x8 qa[C::NC], da[C::NC];
-#pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        qa[c] = *(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]);
-        da[c] = *(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       f32x16 s = f32x16{}, dpv = f32x16{};
+      if constexpr (PART != 2) {
+        bf16x8 qa[C::NC], da[C::NC];
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        s = mfma32(qa[c], kf[c], s);
-        dpv = mfma32(da[c], vf[c], dpv);
+        for (int c = 0; c < C::NC; ++c) {
+          qa[c] = *(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]);
+          if constexpr (WANT_DK) da[c] = *(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < C::NC; ++c) {
+          s = mfma32(qa[c], kf[c], s);
+          if constexpr (WANT_DK) dpv = mfma32(da[c], vf[c], dpv);
+        }
+      } else {
+        // the dK part holds K and V rows: operands stream four reads ahead instead
+        constexpr int LA = 4;
+        auto rd = [&](int j) {
+          return *(const bf16x8*)(((j & 1) ? DO : Q) + 32 * qb * C::ROWB + off.ro[j >> 1]);
+        };
+        bf16x8 opa[LA];
+#pragma unroll
+        for (int j = 0; j < LA; ++j) opa[j] = rd(j);
+#pragma unroll
+        for (int j = 0; j < 2 * C::NC; ++j) {
+          if (j & 1) dpv = mfma32(opa[j % LA], vf[j >> 1], dpv);
+          else s = mfma32(opa[j % LA], kf[j >> 1], s);
+          if (j + LA < 2 * C::NC) opa[j % LA] = rd(j + LA);
+        }
       }
       // rows of s / dpv: query 32qb + 8g + 4h + j, column: this lane's key
       f32x4 L4[4], D4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         L4[g] = *(const f32x4*)(slse[cur] + 32 * qb + 8 * g + 4 * h);
-        D4[g] = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
+        if constexpr (WANT_DK) D4[g] = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
       }
       // raw LSE: -L log2e; a row without any visible key (LSE = -inf) only occurs in
       // tiles that are not full, where the mask below replaces its weights by 0
@@ -237,8 +261,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       bf16x8 pa[2], dsa[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pa[r >> 3][r & 7] = (__bf16)p[r];
-        dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
+        if constexpr (WANT_DV) pa[r >> 3][r & 7] = (__bf16)p[r];
+        if constexpr (WANT_DK) dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
       }
       // dV += P^T dO, dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
 #pragma unroll
@@ -247,26 +271,38 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
         bf16x8 ob[C::NDB], qv[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          ob[db] = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
-                        lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
-          qv[db] = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
-                        lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
+          if constexpr (WANT_DV)
+            ob[db] = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
+                          lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
+          if constexpr (WANT_DK)
+            qv[db] = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
+                          lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          mfma32_agpr(dv[db], pa[tt], ob[db]);
-          mfma32_agpr(dk[db], dsa[tt], qv[db]);
+          // with both accumulators (128 registers at D = 128) they live in AGPRs; a single
+          // one stays in VGPRs, which keeps the register split free
+          if constexpr (PART == 0) {
+            mfma32_agpr(dv[db], pa[tt], ob[db]);
+            mfma32_agpr(dk[db], dsa[tt], qv[db]);
+          } else if constexpr (WANT_DV) {
+            dv[db] = mfma32(pa[tt], ob[db], dv[db]);
+          } else {
+            dk[db] = mfma32(dsa[tt], qv[db], dk[db]);
+          }
         }
       }
     }
   }
 
   if (n_items <= 0) return;  // no query of this block sees these keys: nothing to add
+  if constexpr (PART == 0) {
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db) {
-    mfma_agpr_drain(dk[db]);
-    mfma_agpr_drain(dv[db]);
+    for (int db = 0; db < C::NDB; ++db) {
+      mfma_agpr_drain(dk[db]);
+      mfma_agpr_drain(dv[db]);
+    }
   }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j
   float* dkp = a.dk + b * a.dk_sb + kvh * a.dk_sh;
@@ -279,8 +315,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       if (kr < a.Tk) {
         float* pk = dkp + (int64_t)kr * a.dk_st + 32 * db + lq;
         float* pv = dvp + (int64_t)kr * a.dv_st + 32 * db + lq;
-        *pk += a.scale * dk[db][r];
-        *pv += dv[db][r];
+        if constexpr (WANT_DK) *pk += a.scale * dk[db][r];
+        if constexpr (WANT_DV) *pv += dv[db][r];
       }
     }
 }
@@ -556,10 +592,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   }
 }
 
-template <int D, int NS>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
+template <int D, int NS, int PART>
+__global__ __launch_bounds__(256, PART == 0 ? 1 : 2) void dkdv_kernel(BwdArgs a, int n_kt) {
   __shared__ DkdvLds<D, NS> sm;
-  dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+  dkdv_body<D, NS, PART>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
 template <int D, int NS, int KS>
@@ -585,7 +621,7 @@ __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, 
     const int L = xcd_remap(id, n_dq_pad);
     if (L < n_dq) dq_body<D, NSQ, KSQ>(a, L, n_qt, sm.q);
   } else {
-    dkdv_body<D, NSK>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
+    dkdv_body<D, NSK, 0>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
   }
 }
 
@@ -616,7 +652,19 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     }
   }
   if (which & 1) {
-    hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    // At D = 128 both accumulators together allow one wave per SIMD. With at
+    // least four workgroups per CU the half runs instead as two launches (dV,
+    // then dK) that each hold one accumulator and keep two waves per SIMD; S is
+    // then formed twice more. Smaller grids (grouped heads) keep one launch:
+    // two resident workgroups per CU would leave the heaviest ones as a tail.
+    if (D == 128 && bkv * n_kt >= 1024) {
+      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    } else {
+      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

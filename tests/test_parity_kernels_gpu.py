@@ -451,6 +451,56 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
     assert acc[0].abs().sum() > 0
 
 
+def test_dkdv_two_launch_form_matches_one_launch_and_oracle():
+    # At D = 128 a dK/dV grid of at least 1024 workgroups runs as a dV launch and a dK launch;
+    # smaller grids run one launch holding both accumulators. Both forms take every MFMA chain
+    # in the same order, so 16 heads at once (1024 workgroups of 128 keys) must equal the same
+    # heads two at a time (128 workgroups) bit for bit. Sampled keys are checked against the
+    # oracle: the last keys (every query that sees them is among the last rows) and key 0 of
+    # one head over all 8192 rows.
+    B, H, T, D = 1, 16, 8192, 128
+    log(f"dkdv two-launch form B{B} H{H} T{T} D{D}")
+    q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=131, n=4)
+    m = (T, T, 0, 0)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o = torch.empty(B, H, T, D, device=DEV)
+    lse = torch.empty(B, H, T, device=DEV)
+    cp.cpattn_block_fwd(qd, kd, vd, m, m, o, lse)
+    delta = torch.empty(B, H, T, device=DEV)
+    cp.cpattn_bwd_preprocess(dod, o, delta)
+    dk1 = torch.zeros(B, H, T, D, device=DEV)
+    dv1 = torch.zeros_like(dk1)
+    cp.cpattn_block_bwd_dkdv(qd, kd, vd, dod, lse, delta, dk1, dv1, m, m)
+    dk2 = torch.zeros_like(dk1)
+    dv2 = torch.zeros_like(dk1)
+    for h in range(0, H, 2):
+        sl = slice(h, h + 2)
+        dk_h = torch.zeros(B, 2, T, D, device=DEV)
+        dv_h = torch.zeros_like(dk_h)
+        cp.cpattn_block_bwd_dkdv(qd[:, sl].contiguous(), kd[:, sl].contiguous(), vd[:, sl].contiguous(),
+                                 dod[:, sl].contiguous(), lse[:, sl].contiguous(), delta[:, sl].contiguous(),
+                                 dk_h, dv_h, m, m)
+        dk2[:, sl] = dk_h
+        dv2[:, sl] = dv_h
+    torch.cuda.synchronize()
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    head = 5
+    q64, k64, v64, do64 = (f64(x[:, head:head + 1]) for x in (q, k, v, do))
+    pos = np.arange(T)
+    J = [T - 100, T - 33, T - 1]
+    R = list(range(J[0], T))
+    O, L = oa.block_attention_fwd(q64[:, :, R], k64, v64, R, pos)
+    _, gk, gv = oa.block_attention_bwd(q64[:, :, R], k64[:, :, J], v64[:, :, J], do64[:, :, R], O, L, R, J)
+    O, L = oa.block_attention_fwd(q64, k64, v64, pos, pos)
+    _, gk0, gv0 = oa.block_attention_bwd(q64, k64[:, :, :1], v64[:, :, :1], do64, O, L, pos, [0])
+    got_k = f64(dk1[:, head:head + 1])
+    got_v = f64(dv1[:, head:head + 1])
+    e = (max_err(got_k[:, :, J], gk), max_err(got_v[:, :, J], gv),
+         max_err(got_k[:, :, :1], gk0), max_err(got_v[:, :, :1], gv0))
+    log(f"  sampled keys: dk {e[0]:.3g} dv {e[1]:.3g}; key 0: dk {e[2]:.3g} dv {e[3]:.3g}")
+    assert max(e) <= TOL_BF16
+
+
 # ----------------------------------------------------------------------------- grouped-query attention
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
