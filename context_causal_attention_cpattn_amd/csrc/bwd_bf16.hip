@@ -304,21 +304,32 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       mfma_agpr_drain(dv[db]);
     }
   }
-  // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j
-  float* dkp = a.dk + b * a.dk_sb + kvh * a.dk_sh;
-  float* dvp = a.dv + b * a.dv_sb + kvh * a.dv_sh;
+  // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j. The wave's 32
+  // rows go through a buffer resource bounded at its last key, so rows past Tk read as zero
+  // and drop their stores with no branch. Each accumulator's old values are all read before
+  // its first store: the compiler cannot tell dK from dV apart, so read-add-store pairs in
+  // turn would each wait for a full memory round trip.
+  const int rows = min(32, a.Tk - kw0);
+  auto add_rows = [&](float* base, int64_t st, const f32x16(&acc)[C::NDB], float mul) __attribute__((always_inline)) {
+    const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
+    unsigned old[C::NDB][16];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
+    for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (kr < a.Tk) {
-        float* pk = dkp + (int64_t)kr * a.dk_st + 32 * db + lq;
-        float* pv = dvp + (int64_t)kr * a.dv_st + 32 * db + lq;
-        if constexpr (WANT_DK) *pk += a.scale * dk[db][r];
-        if constexpr (WANT_DV) *pv += dv[db][r];
-      }
-    }
+      for (int r = 0; r < 16; ++r)
+        old[db][r] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db, 0, 0);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * acc[db][r]), rs,
+            (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db, 0, 0);
+  };
+  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale);
+  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -578,16 +589,20 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   }
 
   if (row_ok) {
+    // all old values first, then the stores (one memory round trip)
     float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
+    f32x4 v4[C::NDB][4];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) v4[db][g] = *(const f32x4*)(o + 32 * db + 8 * g + 4 * h);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4* p4 = (f32x4*)(o + 32 * db + 8 * g + 4 * h);
-        f32x4 v4 = *p4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] += a.scale * acc[db][4 * g + j];
-        *p4 = v4;
+        for (int j = 0; j < 4; ++j) v4[db][g][j] += a.scale * acc[db][4 * g + j];
+        *(f32x4*)(o + 32 * db + 8 * g + 4 * h) = v4[db][g];
       }
   }
 }
@@ -657,14 +672,17 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     // then dK) that each hold one accumulator and keep two waves per SIMD; S is
     // then formed twice more. Smaller grids (grouped heads) keep one launch:
     // two resident workgroups per CU would leave the heaviest ones as a tail.
-    if (D == 128 && bkv * n_kt >= 1024) {
-      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-    } else {
-      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    bool two = false;
+    if constexpr (D == 128) {
+      two = bkv * n_kt >= 1024;
+      if (two) {
+        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+      }
     }
+    if (!two) hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

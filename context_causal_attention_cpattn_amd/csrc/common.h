@@ -76,6 +76,12 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& a, const bf16x4& b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Fourth word of a raw buffer resource on this architecture family: data format
+// 32-bit (DATA_FORMAT = 4), every other field zero. With stride 0 an access is
+// in range when its byte offset + size <= num_records; out-of-range loads return
+// zero and out-of-range stores are dropped.
+constexpr int kBufferFlags = 0x00020000;
+
 // LDS tiles of 16-bit elements, D per row, stored without padding. The 16-byte
 // chunk c of row r sits at physical chunk c ^ swz_mask<D>(r). With 64 banks of
 // 4 bytes this is free of bank conflicts for (a) 16-byte reads where 16 lanes

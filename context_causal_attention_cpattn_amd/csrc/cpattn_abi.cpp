@@ -415,6 +415,9 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
   if ((which & 2) && (st = check_tensor(dq_acc, "dq_acc", 4))) return st;
   if ((which & 1) && ((st = check_tensor(dk_acc, "dk_acc", 4)) || (st = check_tensor(dv_acc, "dv_acc", 4))))
     return st;
+  // accumulator rows must not overlap (the dK/dV epilogue bounds a wave's rows by its last key)
+  if (((which & 2) && dq_acc->st < D) || ((which & 1) && (dk_acc->st < D || dv_acc->st < D)))
+    return fail(CPATTN_EINVAL, "accumulator T stride below D (rows overlap)");
   if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
   if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
   BwdArgs a{};

@@ -172,6 +172,13 @@ def test_merge_and_bwd_reject():
     assert lib.cpattn_block_bwd(bt, bt, bt, bt, 0, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1, 1, 64, 64, 64,
                                 ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -2  # fp32 backward
     assert lib.cpattn_bwd_preprocess(bt, 3, bt, ctypes.byref(l3), 1, 1, 64, 64, None) == -1
+    # accumulators whose rows overlap (T stride 32 < D = 64) are refused before any launch
+    ov = ctypes.byref(_t(st=32))
+    assert lib.cpattn_block_bwd(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, ov, 1, 1, 64, 64, 64,
+                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -1
+    assert "overlap" in cp.cpattn_last_error()
+    assert lib.cpattn_block_bwd_dq(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), ov, 1, 1, 64, 64, 64,
+                                   ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -1
 
 
 def test_rope_table_rejects():
