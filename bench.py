@@ -103,9 +103,13 @@ class Share:
         self.o_blk = torch.empty(w.B, w.H, Tl, w.D, **f32)
         self.l_blk = torch.empty(w.B, w.H, Tl, **f32)
         self.delta = torch.empty(w.B, w.H, Tl, **f32)
-        self.dq = torch.zeros(w.B, w.H, Tl, w.D, **f32)
-        self.dk = [torch.zeros(w.B, w.kv_heads, Tl, w.D, **f32) for _ in range(N)]
-        self.dv = [torch.zeros(w.B, w.kv_heads, Tl, w.D, **f32) for _ in range(N)]
+        # the fp32 accumulators are views of one allocation, cleared by one fill per step
+        nq, nkv = w.B * w.H * Tl * w.D, w.B * w.kv_heads * Tl * w.D
+        self.grads = torch.zeros(nq + 2 * N * nkv, **f32)
+        self.dq = self.grads[:nq].view(w.B, w.H, Tl, w.D)
+        kv = self.grads[nq:].view(2 * N, w.B, w.kv_heads, Tl, w.D)
+        self.dk = [kv[i] for i in range(N)]
+        self.dv = [kv[N + i] for i in range(N)]
         # per ring step: (src, row_begin, visible pairs per (b, h))
         self.steps = []
         qp = self.pos[0]
@@ -222,9 +226,7 @@ class Share:
         """One pass of the hot path. ``ev(name, work)`` returns a context that brackets one launch."""
         rec = ev if ev is not None else _no_event
         if self.do_bwd:
-            self.dq.zero_()
-            for x in self.dk + self.dv:
-                x.zero_()
+            self.grads.zero_()
         for name, work, fn, args in self.plan:
             with rec(name, work):
                 status = fn(*args)
