@@ -619,24 +619,26 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
   dq_body<D, NS, KS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
 }
 
-// Both halves of the block backward in one grid: the first n_dq workgroups (a
-// multiple of 8, the surplus idle) form dQ, the rest dK/dV. The two write
-// disjoint outputs, and sharing a grid lets them fill the chip together when
-// each alone is too small to. Workgroups are dealt to the 8 XCDs round-robin by
-// id, so both roles land on every XCD; within a role the ids are remapped as in
-// the single-role kernels.
+// Both halves of the block backward in one grid: the first n_kv workgroups
+// (padded to a multiple of 8, the surplus idle) form dK/dV, the rest dQ. The two
+// write disjoint outputs, and sharing a grid lets them fill the chip together
+// when each alone is too small to. dK/dV workgroups are the longer ones (their
+// keys see the query tiles one after another), so they take the low ids, which
+// are dispatched first, and the short dQ workgroups fill the slots they leave.
+// Workgroups are dealt to the 8 XCDs round-robin by id, so both roles land on
+// every XCD; within a role the ids are remapped as in the single-role kernels.
 template <int D, int NSK, int NSQ, int KSQ>
-__global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_dq, int n_dq_pad) {
+__global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_kv, int n_kv_pad) {
   __shared__ union {
     DkdvLds<D, NSK> kv;
     DqLds<D, NSQ, KSQ> q;
   } sm;
   const int id = blockIdx.x;
-  if (id < n_dq_pad) {
-    const int L = xcd_remap(id, n_dq_pad);
-    if (L < n_dq) dq_body<D, NSQ, KSQ>(a, L, n_qt, sm.q);
+  if (id < n_kv_pad) {
+    const int L = xcd_remap(id, n_kv_pad);
+    if (L < n_kv) dkdv_body<D, NSK, 0>(a, L, n_kt, sm.kv);
   } else {
-    dkdv_body<D, NSK, 0>(a, xcd_remap(id - n_dq_pad, gridDim.x - n_dq_pad), n_kt, sm.kv);
+    dq_body<D, NSQ, KSQ>(a, xcd_remap(id - n_kv_pad, gridDim.x - n_kv_pad), n_qt, sm.q);
   }
 }
 
@@ -655,14 +657,14 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     // both kernels keep two workgroups per CU at this width, so one grid costs nothing
     if (which == 3) {
       const int nq = split ? n_qt2 : n_qt;
-      const int64_t n_dq = bh * nq, n_dq_pad = (n_dq + 7) / 8 * 8;
-      const int64_t grid = n_dq_pad + bkv * n_kt;
+      const int64_t n_kv = bkv * n_kt, n_kv_pad = (n_kv + 7) / 8 * 8;
+      const int64_t grid = n_kv_pad + bh * nq;
       if (split)
         hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 2>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
-                           nq, (int)n_dq, (int)n_dq_pad);
+                           nq, (int)n_kv, (int)n_kv_pad);
       else
         hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 1>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
-                           nq, (int)n_dq, (int)n_dq_pad);
+                           nq, (int)n_kv, (int)n_kv_pad);
       return hipGetLastError();
     }
   }
