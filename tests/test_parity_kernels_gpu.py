@@ -501,6 +501,49 @@ def test_dkdv_two_launch_form_matches_one_launch_and_oracle():
     assert max(e) <= TOL_BF16
 
 
+def test_small_grid_splits_match_large_grid_forms_and_oracle():
+    # At 64-wide heads a backward grid under two workgroups per CU splits each dQ
+    # workgroup's keys between two wave pairs, and, on a causal block whose longest chain
+    # of query tiles is 1.5x the mean (here 16 tiles against 9), each dK/dV workgroup's
+    # query tiles; the pairs' partials are summed. 64 heads (512 workgroups per half)
+    # take the unsplit forms, the same heads eight at a time the split ones. The forms
+    # add the same terms in another order, so they agree to fp32 rounding; two heads are
+    # checked against the oracle.
+    B, H, T, D = 1, 64, 1024, 64
+    log(f"split vs unsplit backward B{B} H{H} T{T} D{D}")
+    q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=151, n=4)
+    m = (T, T, 0, 0)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    o = torch.empty(B, H, T, D, device=DEV)
+    lse = torch.empty(B, H, T, device=DEV)
+    cp.cpattn_block_fwd(qd, kd, vd, m, m, o, lse)
+    delta = torch.empty(B, H, T, device=DEV)
+    cp.cpattn_bwd_preprocess(dod, o, delta)
+    big = [torch.zeros(B, H, T, D, device=DEV) for _ in range(3)]
+    cp.cpattn_block_bwd(qd, kd, vd, dod, lse, delta, big[0], big[1], big[2], m, m)
+    small = [torch.zeros_like(big[0]) for _ in range(3)]
+    for h in range(0, H, 8):
+        sl = slice(h, h + 8)
+        part = [torch.zeros(B, 8, T, D, device=DEV) for _ in range(3)]
+        cp.cpattn_block_bwd(*(x[:, sl].contiguous() for x in (qd, kd, vd, dod, lse, delta)), *part, m, m)
+        for x, y in zip(small, part):
+            x[:, sl] = y
+    torch.cuda.synchronize()
+    for x, y, name in zip(big, small, ("dq", "dk", "dv")):
+        err = (x - y).abs().max().item()
+        scale = y.abs().max().item()
+        log(f"  {name}: max |unsplit - split| {err:.3g} (max |split| {scale:.3g})")
+        assert 0 < err <= 1e-5 * max(scale, 1.0)  # other forms: not bitwise equal, but close
+    pos = np.arange(T)
+    for head in (0, 41):
+        q64, k64, v64, do64 = (f64(x[:, head:head + 1]) for x in (q, k, v, do))
+        O, L = oa.block_attention_fwd(q64, k64, v64, pos, pos)
+        g = oa.block_attention_bwd(q64, k64, v64, do64, O, L, pos, pos)
+        for got in (big, small):
+            e = max(max_err(f64(t[:, head:head + 1]), r) for t, r in zip(got, g))
+            assert e <= TOL_BF16, (head, e)
+
+
 # ----------------------------------------------------------------------------- grouped-query attention
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
