@@ -103,13 +103,17 @@ class Share:
         self.o_blk = torch.empty(w.B, w.H, Tl, w.D, **f32)
         self.l_blk = torch.empty(w.B, w.H, Tl, **f32)
         self.delta = torch.empty(w.B, w.H, Tl, **f32)
-        # the fp32 accumulators are views of one allocation, cleared by one fill per step
+        # The fp32 accumulators are views of one allocation. dQ and the own block's dK/dV
+        # take their first contribution at step 0 with accumulate = 0 (overwrite); the
+        # other blocks' dK/dV stand for partial sums that would arrive with their blocks
+        # in a real ring, and are cleared by one fill per step here.
         nq, nkv = w.B * w.H * Tl * w.D, w.B * w.kv_heads * Tl * w.D
         self.grads = torch.zeros(nq + 2 * N * nkv, **f32)
         self.dq = self.grads[:nq].view(w.B, w.H, Tl, w.D)
         kv = self.grads[nq:].view(2 * N, w.B, w.kv_heads, Tl, w.D)
-        self.dk = [kv[i] for i in range(N)]
-        self.dv = [kv[N + i] for i in range(N)]
+        self.dk = [kv[0]] + [kv[2 + i] for i in range(N - 1)]
+        self.dv = [kv[1]] + [kv[N + 1 + i] for i in range(N - 1)]
+        self.foreign = self.grads[nq + 2 * nkv:]
         # per ring step: (src, row_begin, visible pairs per (b, h))
         self.steps = []
         qp = self.pos[0]
@@ -178,9 +182,10 @@ class Share:
         if do_bwd:
             plan.append(("bwd_preprocess", self.bh * Tl * (D * 2 + D * 4 + 4), lib.cpattn_bwd_preprocess,
                          (by(do), bf16, by(o), by(delta), B, H, Tl, D, st)))
-            for src, rb, pairs in self.steps:
+            for s, (src, rb, pairs) in enumerate(self.steps):
                 if rb >= Tl:
                     continue
+                acc = 0 if s == 0 else 1  # the own block's contribution comes first
                 k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
                 dk, dv = T(self.dk[src]), T(self.dv[src])
                 keep += [k, v, km, dk, dv]
@@ -192,19 +197,19 @@ class Share:
                 if gqa:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd_gqa,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
-                                  B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, st)))
+                                  B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, acc, st)))
                     continue
                 if not split_bwd:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
-                                  B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, st)))
+                                  B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, acc, st)))
                     continue
                 plan.append(("block_bwd_dkdv", 8 * D * pairs * self.bh, lib.cpattn_block_bwd_dkdv,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dk), by(dv), B, H, Tl, Tk, D,
-                              by(qm), by(km), 1, 0.0, st)))
+                              by(qm), by(km), 1, 0.0, acc, st)))
                 plan.append(("block_bwd_dq", 6 * D * pairs * self.bh, lib.cpattn_block_bwd_dq,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), B, H, Tl, Tk, D, by(qm),
-                              by(km), 1, 0.0, st)))
+                              by(km), 1, 0.0, acc, st)))
             if self.tab is not None:
                 # gradients back through R^T once: dQ, then every dK block (fp32 read and written,
                 # the table row of each position once)
@@ -225,8 +230,8 @@ class Share:
     def step(self, ev=None):
         """One pass of the hot path. ``ev(name, work)`` returns a context that brackets one launch."""
         rec = ev if ev is not None else _no_event
-        if self.do_bwd:
-            self.grads.zero_()
+        if self.do_bwd and self.foreign.numel():
+            self.foreign.zero_()
         for name, work, fn, args in self.plan:
             with rec(name, work):
                 status = fn(*args)

@@ -72,17 +72,17 @@ _SIGS = {
     "cpattn_block_fwd_gqa": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32, _f32,
                                             _vp, _i64, _i64, _i64, _T, _T, _vp]),
     "cpattn_block_bwd_gqa": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64,
-                                            _i64, _M, _M, _i32, _f32, _vp]),
+                                            _i64, _M, _M, _i32, _f32, _i32, _vp]),
     "cpattn_ring_fwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64, ctypes.c_int32]),
     "cpattn_ring_fwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _vp, _i64, _T, _T, _vp, ctypes.c_size_t, _vp]),
     "cpattn_bwd_preprocess": (ctypes.c_int, [_T, _i32, _T, _T, _i64, _i64, _i64, _i64, _vp]),
     "cpattn_block_bwd": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M,
-                                        _M, _i32, _f32, _vp]),
+                                        _M, _i32, _f32, _i32, _vp]),
     "cpattn_block_bwd_dkdv": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M,
-                                             _M, _i32, _f32, _vp]),
+                                             _M, _i32, _f32, _i32, _vp]),
     "cpattn_block_bwd_dq": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M, _M,
-                                           _i32, _f32, _vp]),
+                                           _i32, _f32, _i32, _vp]),
 }
 
 _lib = None
@@ -244,30 +244,32 @@ def cpattn_bwd_preprocess(dout, o, delta, stream=None):
 
 
 def cpattn_block_bwd(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
-                     scale: float = 0.0, stream=None):
+                     scale: float = 0.0, accumulate: bool = True, stream=None):
     B, H, Tq, D = q.shape
     Tk = k.shape[2]
     _check(load().cpattn_block_bwd(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                    _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq, Tk,
-                                   D, _map(qmap), _map(kmap), int(causal), float(scale), _stream(stream)))
+                                   D, _map(qmap), _map(kmap), int(causal), float(scale), int(accumulate),
+                                   _stream(stream)))
 
 
 def cpattn_block_bwd_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
-                          scale: float = 0.0, stream=None):
+                          scale: float = 0.0, accumulate: bool = True, stream=None):
     B, H, Tq, D = q.shape
     Tk = k.shape[2]
     _check(load().cpattn_block_bwd_dkdv(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q),
                                         _tensor(lse, 3), _tensor(delta, 3), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq,
-                                        Tk, D, _map(qmap), _map(kmap), int(causal), float(scale), _stream(stream)))
+                                        Tk, D, _map(qmap), _map(kmap), int(causal), float(scale), int(accumulate),
+                                        _stream(stream)))
 
 
 def cpattn_block_bwd_dq(q, k, v, dout, lse, delta, dq_acc, qmap, kmap, causal: bool = True, scale: float = 0.0,
-                        stream=None):
+                        accumulate: bool = True, stream=None):
     B, H, Tq, D = q.shape
     Tk = k.shape[2]
     _check(load().cpattn_block_bwd_dq(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                       _tensor(delta, 3), _tensor(dq_acc), B, H, Tq, Tk, D, _map(qmap), _map(kmap),
-                                      int(causal), float(scale), _stream(stream)))
+                                      int(causal), float(scale), int(accumulate), _stream(stream)))
 
 
 def cpattn_block_fwd_gqa(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: float = 0.0, rope_table=None,
@@ -283,11 +285,11 @@ def cpattn_block_fwd_gqa(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale
 
 
 def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
-                         scale: float = 0.0, stream=None):
+                         scale: float = 0.0, accumulate: bool = True, stream=None):
     """Grouped-query block backward: dk_acc / dv_acc per KV head, summed over each group."""
     B, H, Tq, D = q.shape
     H_kv, Tk = k.shape[1], k.shape[2]
     _check(load().cpattn_block_bwd_gqa(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                        _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H,
                                        H_kv, Tq, Tk, D, _map(qmap), _map(kmap), int(causal), float(scale),
-                                       _stream(stream)))
+                                       int(accumulate), _stream(stream)))

@@ -314,7 +314,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 
   for (int e = n_j; e < n_jmax; ++e) __syncthreads();  // a share with fewer items pads
 
-  if (n_items <= 0) return;  // no query of this block sees these keys: nothing to add
+  // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
+  if (n_items <= 0 && a.acc) return;
   if constexpr (PART == 0) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -322,9 +323,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       mfma_agpr_drain(dv[db]);
     }
   }
+  // QS = 2: the odd share stages its dK/dV partials in LDS (same keys, same layout) and
+  // the even share adds them element by element as it stores, so the accumulators are
+  // never copied out of their registers.
+  constexpr int NV = (WANT_DK ? C::NDB * 16 : 0) + (WANT_DV ? C::NDB * 16 : 0);
+  constexpr int DV0 = WANT_DK ? C::NDB * 16 : 0;  // first dV slot of a wave's staging
+  const float* part = nullptr;
   if constexpr (QS == 2) {
-    // ---- add the odd share's dK/dV partials to the even share's (same keys, same layout)
-    constexpr int NV = (WANT_DK ? C::NDB * 16 : 0) + (WANT_DV ? C::NDB * 16 : 0);
     static_assert(NR * NV * 64 * 4 <= sizeof(sm), "staging fits the rings");
     float* cb = (float*)&sm + rb * NV * 64;
     __syncthreads();  // every wave is done with its rings
@@ -334,18 +339,12 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           if constexpr (WANT_DK) cb[(16 * db + r) * 64 + l] = dk[db][r];
-          if constexpr (WANT_DV) cb[((WANT_DK ? C::NDB * 16 : 0) + 16 * db + r) * 64 + l] = dv[db][r];
+          if constexpr (WANT_DV) cb[(DV0 + 16 * db + r) * 64 + l] = dv[db][r];
         }
     }
     __syncthreads();
     if (qh == 1) return;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (WANT_DK) dk[db][r] += cb[(16 * db + r) * 64 + l];
-        if constexpr (WANT_DV) dv[db][r] += cb[((WANT_DK ? C::NDB * 16 : 0) + 16 * db + r) * 64 + l];
-      }
+    part = cb;
   }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j. The wave's 32
   // rows go through a buffer resource bounded at its last key, so rows past Tk read as zero
@@ -353,26 +352,31 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   // its first store: the compiler cannot tell dK from dV apart, so read-add-store pairs in
   // turn would each wait for a full memory round trip.
   const int rows = min(32, a.Tk - kw0);
-  auto add_rows = [&](float* base, int64_t st, const f32x16(&acc)[C::NDB], float mul) __attribute__((always_inline)) {
+  auto add_rows = [&](float* base, int64_t st, const f32x16(&acc)[C::NDB], float mul, int slot0)
+                      __attribute__((always_inline)) {
     const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
+    // an overwrite reads through an empty range: every read returns 0 and touches no memory
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, a.acc ? bytes : 0,
+                                                      kBufferFlags);
+    auto offset = [&](int db, int r) { return (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db; };
     unsigned old[C::NDB][16];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        old[db][r] = __builtin_amdgcn_raw_buffer_load_b32(
-            rs, (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db, 0, 0);
+      for (int r = 0; r < 16; ++r) old[db][r] = __builtin_amdgcn_raw_buffer_load_b32(rl, offset(db, r), 0, 0);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_buffer_store_b32(
-            __builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * acc[db][r]), rs,
-            (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        float x = acc[db][r];
+        if constexpr (QS == 2) x += part[(slot0 + 16 * db + r) * 64 + l];
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * x),
+                                              rs, offset(db, r), 0, 0);
+      }
   };
-  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale);
-  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f);
+  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale, 0);
+  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f, DV0);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -423,7 +427,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   const int last_row = (q0 + ROWS < a.Tq ? q0 + ROWS : a.Tq) - 1;
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
   const int n_kt = (n_vis + kKB - 1) / kKB;
-  if (n_kt == 0) return;  // no key of this block is visible to these rows: nothing to add
+  if (n_kt == 0) {  // no key of this block is visible to these rows: nothing to add
+    if (!a.acc && kh == 0 && row_ok) {  // an overwrite writes zeros
+      float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(f32x4*)(o + 32 * db + 8 * g + 4 * h) = f32x4{};
+    }
+    return;
+  }
   const int n_jmax = (n_kt + KS - 1) / KS;                    // tiles of the larger share
   const int n_j = n_kt > kh ? (n_kt - kh + KS - 1) / KS : 0;  // tiles of this wave's share
   auto tile = [&](int j) { return KS * j + kh; };
@@ -631,21 +644,30 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
       for (int r = 0; r < 16; ++r) acc[db][r] += cb[(16 * db + r) * 64 + l];
   }
 
-  if (row_ok) {
-    // all old values first, then the stores (one memory round trip)
-    float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
-    f32x4 v4[C::NDB][4];
+  {
+    // The wave's 32 rows go through a buffer resource bounded at its last row (rows past
+    // Tq read as zero and drop their stores); all old values are read before the stores
+    // (one memory round trip), through an empty range when overwriting.
+    const int w_row0 = q0 + 32 * rb;
+    const int wrows = min(32, a.Tq - w_row0);
+    float* base = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)w_row0 * a.dq_st;
+    const int bytes = wrows > 0 ? ((wrows - 1) * (int)a.dq_st + D) * 4 : 0;  // rows never overlap: st >= D
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kBufferFlags);
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, a.acc ? bytes : 0, kBufferFlags);
+    auto offset = [&](int db, int g) { return (int)((lq * a.dq_st + 32 * db + 8 * g + 4 * h) * 4); };
+    u32x4 old[C::NDB][4];
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) v4[db][g] = *(const f32x4*)(o + 32 * db + 8 * g + 4 * h);
+      for (int g = 0; g < 4; ++g) old[db][g] = __builtin_amdgcn_raw_buffer_load_b128(rl, offset(db, g), 0, 0);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = __builtin_bit_cast(f32x4, old[db][g]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v4[db][g][j] += a.scale * acc[db][4 * g + j];
-        *(f32x4*)(o + 32 * db + 8 * g + 4 * h) = v4[db][g];
+        for (int j = 0; j < 4; ++j) v4[j] += a.scale * acc[db][4 * g + j];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), rs, offset(db, g), 0, 0);
       }
   }
 }

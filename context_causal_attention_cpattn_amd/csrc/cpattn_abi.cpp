@@ -403,7 +403,7 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
                int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
                const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq,
                int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-               float scale, int which, void* stream, const char* what, int64_t H_kv) {
+               float scale, int32_t accumulate, int which, void* stream, const char* what, int64_t H_kv) {
   int st, G;
   if ((st = check_dims(B, H, Tq, Tk, D))) return st;
   if ((st = group_of(H, H_kv, &G))) return st;
@@ -420,6 +420,7 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
     return fail(CPATTN_EINVAL, "accumulator T stride below D (rows overlap)");
   if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
   if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
+  if (accumulate != 0 && accumulate != 1) return fail(CPATTN_EINVAL, "accumulate must be 0 or 1");
   BwdArgs a{};
   a.q = view(q), a.k = view(k), a.v = view(v), a.dout = view(dout);
   a.lse = view(lse), a.delta = view(delta);
@@ -433,6 +434,7 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
   a.causal = causal != 0;
   a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
   a.G = G;
+  a.acc = accumulate;
   return launch_status(launch_bwd_bf16(a, which, (hipStream_t)stream), what);
 }
 
@@ -445,36 +447,38 @@ int cpattn_block_bwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const c
                          const cpattn_tensor* delta, const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc,
                          const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
                          int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-                         float scale, void* stream) {
+                         float scale, int32_t accumulate, void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 3, stream, "block_bwd_gqa", H_kv);
+                    scale, accumulate, 3, stream, "block_bwd_gqa", H_kv);
 }
 
 int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                      const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
                      const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
                      int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
-                     const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+                     const cpattn_posmap* kmap, int32_t causal, float scale, int32_t accumulate,
+                     void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 3, stream, "block_bwd", H);
+                    scale, accumulate, 3, stream, "block_bwd", H);
 }
 
 int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                           const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
                           const cpattn_tensor* delta, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
                           int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
-                          const cpattn_posmap* kmap, int32_t causal, float scale, void* stream) {
+                          const cpattn_posmap* kmap, int32_t causal, float scale, int32_t accumulate,
+                          void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, nullptr, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 1, stream, "block_bwd_dkdv", H);
+                    scale, accumulate, 1, stream, "block_bwd_dkdv", H);
 }
 
 int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                         const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
                         const cpattn_tensor* dq_acc, int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
                         const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
-                        void* stream) {
+                        int32_t accumulate, void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, nullptr, nullptr, B, H, Tq, Tk, D, qmap, kmap, causal,
-                    scale, 2, stream, "block_bwd_dq", H);
+                    scale, accumulate, 2, stream, "block_bwd_dq", H);
 }
 
 }  // extern "C"

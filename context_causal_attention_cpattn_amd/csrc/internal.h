@@ -65,6 +65,7 @@ struct BwdArgs {
   int causal;
   float scale;
   int G;  // query heads per KV head; dK / dV are per KV head, summed over its group
+  int acc;  // 1: add into the accumulators; 0: overwrite them (zeros where no pair contributes)
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

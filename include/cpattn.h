@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 2
+#define CPATTN_ABI_VERSION 3
 
 enum {
   CPATTN_OK = 0,
@@ -258,8 +258,13 @@ int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn
  *   dq_acc += scale * dS k
  *   dk_acc += scale * dS^T q
  * dq_acc is [B,H,Tq,D] (the local rows), dk_acc and dv_acc are [B,H,Tk,D]
- * (the block's rows). The caller zeroes them once before the first step and
- * never between steps. bf16 inputs only; rotary is not supported here.
+ * (the block's rows); their T stride must be at least D (rows never overlap).
+ * accumulate = 1 adds as above: the caller zeroes the accumulators once and
+ * never between steps. accumulate = 0 overwrites them instead: every row is
+ * written, with this block's contribution or 0 where no pair contributes, so
+ * the first contribution to an accumulator needs no clearing beforehand (the
+ * rank's own diagonal block, which every local row and key takes part in).
+ * Other values: EINVAL. bf16 inputs only; rotary is not supported here.
  * Two halves (key-tile-major for dk/dv, query-tile-major for dq), no atomics:
  * results are bitwise reproducible and equal to calling the two halves below.
  * At D = 64 both halves share one grid, so that a small block still fills the
@@ -272,7 +277,7 @@ int cpattn_block_bwd(const cpattn_tensor* q, const cpattn_tensor* k, const cpatt
                      const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
                      int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
                      const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-                     float scale, void* stream);
+                     float scale, int32_t accumulate, void* stream);
 
 /*
  * Grouped-query form of cpattn_block_bwd: q, dout, lse, delta and dq_acc have
@@ -289,10 +294,11 @@ int cpattn_block_bwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const c
                          const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc,
                          int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
                          const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-                         float scale, void* stream);
+                         float scale, int32_t accumulate, void* stream);
 
 /*
- * The two halves of cpattn_block_bwd, same arguments and accumulate semantics:
+ * The two halves of cpattn_block_bwd, same arguments and accumulate semantics
+ * (accumulate applies to the accumulators the half writes):
  * _dkdv adds into dk_acc and dv_acc only (key-tile-major kernel), _dq adds
  * into dq_acc only (query-tile-major kernel). In a real ring the dK/dV
  * partials travel back to their owner while dQ stays local (BluScriptCP log,
@@ -306,12 +312,13 @@ int cpattn_block_bwd_dkdv(const cpattn_tensor* q, const cpattn_tensor* k, const 
                           const cpattn_tensor* delta, const cpattn_tensor* dk_acc,
                           const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq, int64_t Tk,
                           int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap,
-                          int32_t causal, float scale, void* stream);
+                          int32_t causal, float scale, int32_t accumulate, void* stream);
 int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
                         const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
                         const cpattn_tensor* delta, const cpattn_tensor* dq_acc, int64_t B, int64_t H,
                         int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
-                        const cpattn_posmap* kmap, int32_t causal, float scale, void* stream);
+                        const cpattn_posmap* kmap, int32_t causal, float scale, int32_t accumulate,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 2
+    assert cp.cpattn_version() == 3
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -170,15 +170,22 @@ def test_merge_and_bwd_reject():
     m = cp.cpattn_posmap(64, 64, 0, 0)
     bt = ctypes.byref(t)
     assert lib.cpattn_block_bwd(bt, bt, bt, bt, 0, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1, 1, 64, 64, 64,
-                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -2  # fp32 backward
+                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, 1, None) == -2  # fp32 backward
     assert lib.cpattn_bwd_preprocess(bt, 3, bt, ctypes.byref(l3), 1, 1, 64, 64, None) == -1
     # accumulators whose rows overlap (T stride 32 < D = 64) are refused before any launch
     ov = ctypes.byref(_t(st=32))
     assert lib.cpattn_block_bwd(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, ov, 1, 1, 64, 64, 64,
-                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -1
+                                ctypes.byref(m), ctypes.byref(m), 1, 0.0, 1, None) == -1
     assert "overlap" in cp.cpattn_last_error()
     assert lib.cpattn_block_bwd_dq(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), ov, 1, 1, 64, 64, 64,
-                                   ctypes.byref(m), ctypes.byref(m), 1, 0.0, None) == -1
+                                   ctypes.byref(m), ctypes.byref(m), 1, 0.0, 1, None) == -1
+    # accumulate is 0 (overwrite) or 1 (add); anything else is refused before any launch
+    for acc in (2, -1):
+        assert lib.cpattn_block_bwd(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1, 1, 64, 64,
+                                    64, ctypes.byref(m), ctypes.byref(m), 1, 0.0, acc, None) == -1
+        assert "accumulate" in cp.cpattn_last_error()
+        assert lib.cpattn_block_bwd_dkdv(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, 1, 1, 64, 64,
+                                         64, ctypes.byref(m), ctypes.byref(m), 1, 0.0, acc, None) == -1
 
 
 def test_rope_table_rejects():
@@ -232,6 +239,6 @@ def test_gqa_rejects_group_mismatch():
     assert fwd(4, 0) == -1
     assert fwd(2, 4) == -1
     bwd = lambda H, H_kv: lib.cpattn_block_bwd_gqa(bt, bt, bt, bt, 1, ctypes.byref(l3), ctypes.byref(l3), bt, bt, bt, 1,
-                                                   H, H_kv, 64, 64, 64, bm, bm, 1, 0.0, None)
+                                                   H, H_kv, 64, 64, 64, bm, bm, 1, 0.0, 1, None)
     assert bwd(6, 4) == -1
     assert bwd(3, -1) == -1

@@ -544,6 +544,51 @@ def test_small_grid_splits_match_large_grid_forms_and_oracle():
             assert e <= TOL_BF16, (head, e)
 
 
+@pytest.mark.parametrize("form", ["whole", "halves", "gqa"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_overwrite_equals_add_into_zeros(D, form):
+    # accumulate = 0 writes every accumulator row: this block's contribution, or 0 where
+    # no pair contributes. Keys sit at positions Tq/2 .. Tq/2 + Tk - 1, so the first
+    # Tq/2 query rows see no key and the keys past the last query position are seen by
+    # no row; the sizes are ragged. Accumulators full of NaN, overwritten, must equal
+    # zeroed ones added into, bit for bit.
+    B, H, Tq, Tk = 1, 4, 300, 250
+    H_kv = 2 if form == "gqa" else H
+    log(f"overwrite D={D} {form}")
+    q, do = draw_shape(B, H, Tq, D, torch.bfloat16, seed=171, n=2)
+    k, v = draw_shape(B, H_kv, Tk, D, torch.bfloat16, seed=172, n=2)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    qm, km = (Tq, Tq, 0, 0), (Tk, Tk, Tq // 2, Tq // 2)
+    lse, = draw_shape(1, B, H, Tq, torch.float32, seed=173, n=1)
+    delta, = draw_shape(1, B, H, Tq, torch.float32, seed=174, n=1)
+    lse = (lse[0] + 6.0).to(DEV)   # keep exp(s - lse) moderate
+    delta = delta[0].to(DEV)
+
+    def run(init, acc):
+        g = [torch.full((B, H, Tq, D), init, device=DEV), torch.full((B, H_kv, Tk, D), init, device=DEV),
+             torch.full((B, H_kv, Tk, D), init, device=DEV)]
+        if form == "whole":
+            cp.cpattn_block_bwd(qd, kd, vd, dod, lse, delta, *g, qm, km, accumulate=acc)
+        elif form == "halves":
+            cp.cpattn_block_bwd_dkdv(qd, kd, vd, dod, lse, delta, g[1], g[2], qm, km, accumulate=acc)
+            cp.cpattn_block_bwd_dq(qd, kd, vd, dod, lse, delta, g[0], qm, km, accumulate=acc)
+        else:
+            cp.cpattn_block_bwd_gqa(qd, kd, vd, dod, lse, delta, *g, qm, km, accumulate=acc)
+        torch.cuda.synchronize()
+        return g
+
+    over = run(float("nan"), False)
+    added = run(0.0, True)
+    for a_, b_, name in zip(over, added, ("dq", "dk", "dv")):
+        assert torch.equal(a_, b_), name
+    # rows without a visible key and keys no row sees are exactly zero; the rest is not
+    assert over[0][:, :, :Tq // 2].abs().max().item() == 0.0
+    assert over[0][:, :, Tq // 2:].abs().max().item() > 0.0
+    unseen = Tq - Tq // 2  # keys at positions >= Tq
+    assert over[1][:, :, unseen:].abs().max().item() == 0.0 and over[2][:, :, unseen:].abs().max().item() == 0.0
+    assert over[1][:, :, :unseen].abs().max().item() > 0.0
+
+
 # ----------------------------------------------------------------------------- grouped-query attention
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
