@@ -73,47 +73,36 @@ struct Offs {
 // ------------------------------------------------------------------ dK / dV
 constexpr int kKeysPerWG = 32 * kNW;  // 128
 
-// QS query shares, each with its own rings of NS stages
-template <int D, int NS, int QS>
+template <int D, int NS>
 struct DkdvLds {
-  alignas(1024) char sq[QS][NS][BCfg<D>::TILEB];
-  alignas(1024) char sdo[QS][NS][BCfg<D>::TILEB];
-  alignas(16) float slse[QS][NS][kTile];
-  alignas(16) float sdelta[QS][NS][kTile];
+  alignas(1024) char sq[NS][BCfg<D>::TILEB];
+  alignas(1024) char sdo[NS][BCfg<D>::TILEB];
+  alignas(16) float slse[NS][kTile];
+  alignas(16) float sdelta[NS][kTile];
 };
 
 // Workgroup Lg of the dK/dV grid (Lg = bh * n_kt + key tile).
-// QS = 2 splits the query tiles of a workgroup between two pairs of waves that own
-// the same 64 keys (even items to waves 0-1, odd items to waves 2-3, each pair with
-// its own rings); the odd pair's dK/dV partials are added to the even pair's through
-// LDS at the end. This halves the chain of tiles one workgroup walks.
 // PART selects what one launch forms: 0 both dK and dV, 1 dV only (no V rows, no dP),
 // 2 dK only. A launch of one part keeps one accumulator, which brings the 128-wide
 // kernel within two waves per SIMD at the price of forming S in both launches.
-template <int D, int NS, int PART, int QS>
-__device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, DkdvLds<D, NS, QS>& sm) {
+template <int D, int NS, int PART>
+__device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, DkdvLds<D, NS>& sm) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using C = BCfg<D>;
-  static_assert(QS == 1 || QS == 2, "query shares");
-  constexpr int NR = kNW / QS;      // waves per query share (one 32-key block each)
-  constexpr int NIQ = C::NI * QS;   // direct loads per wave per tile (Q or dO)
-  constexpr int LROWS = kTile / NR; // LSE / delta rows each wave of a share brings
+  auto& sq = sm.sq;
+  auto& sdo = sm.sdo;
+  auto& slse = sm.slse;
+  auto& sdelta = sm.sdelta;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const int rb = w % NR;  // key block of the wave
-  const int qh = w / NR;  // query share: items qh, qh + QS, ...
-  auto& sq = sm.sq[qh];
-  auto& sdo = sm.sdo[qh];
-  auto& slse = sm.slse[qh];
-  auto& sdelta = sm.sdelta[qh];
   const int bh = Lg / n_kt;  // (b, KV head)
   const int kt = Lg - bh * n_kt;
   const int H_kv = a.H / a.G;
   const int b = bh / H_kv, kvh = bh - b * H_kv;
-  const int kc0 = kt * (32 * NR);          // first key of the workgroup
-  const int kw0 = kc0 + 32 * rb;           // first key of the wave
+  const int kc0 = kt * kKeysPerWG;         // first key of the workgroup
+  const int kw0 = kc0 + 32 * w;            // first key of the wave
   const int key = kw0 + lq;                // this lane's key
   const bool key_ok = key < a.Tk;
 
@@ -149,19 +138,19 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   const int n_items = n * a.G;    // (query head of the group, tile), head-major
   const float sl2 = a.scale * kLog2e;
 
-  int ld_row[NIQ], ld_col[NIQ];
-  unsigned qo[NIQ], oo[NIQ];
+  int ld_row[C::NI], ld_col[C::NI];
+  unsigned qo[C::NI], oo[C::NI];
 #pragma unroll
-  for (int i = 0; i < NIQ; ++i) {
-    const int p = (rb * NIQ + i) * 64 + l;
+  for (int i = 0; i < C::NI; ++i) {
+    const int p = (w * C::NI + i) * 64 + l;
     ld_row[i] = p / C::CPR;
     ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
     qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
     oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
   }
-  // LSE and delta rows of a tile: every wave of the share brings LROWS of the 64
-  const unsigned lo_lse = (unsigned)((LROWS * rb + (l % LROWS)) * a.lse.st * 4);
-  const unsigned lo_dl = (unsigned)((LROWS * rb + (l % LROWS)) * a.delta.st * 4);
+  // LSE and delta rows of a tile: every wave brings 16 of the 64 (lanes 0..15)
+  const unsigned lo_lse = (unsigned)((16 * w + (l & 15)) * a.lse.st * 4);
+  const unsigned lo_dl = (unsigned)((16 * w + (l & 15)) * a.delta.st * 4);
   // item it = (query head kvh*G + it/n, tile t_begin + it%n)
   auto issue_tile = [&](int it, int buf) {
     const int hq = kvh * a.G + it / n;
@@ -175,25 +164,25 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
     const bool tail = q0 + kTile > a.Tq;  // rows past the end repeat the last row (masked)
 #pragma unroll
-    for (int i = 0; i < NIQ; ++i) {
+    for (int i = 0; i < C::NI; ++i) {
       unsigned q_off = qo[i], o_off = oo[i];
       if (tail) {
         const int r = min(ld_row[i], a.Tq - 1 - q0);
         q_off = (unsigned)((r * a.q.st + ld_col[i]) * 2);
         o_off = (unsigned)((r * a.dout.st + ld_col[i]) * 2);
       }
-      load_lds16(qbase, q_off, sq[buf] + (rb * NIQ + i) * 1024);
-      load_lds16(obase, o_off, sdo[buf] + (rb * NIQ + i) * 1024);
+      load_lds16(qbase, q_off, sq[buf] + (w * C::NI + i) * 1024);
+      load_lds16(obase, o_off, sdo[buf] + (w * C::NI + i) * 1024);
     }
-    if (l < LROWS) {
+    if (l < 16) {
       unsigned l_off = lo_lse, d_off = lo_dl;
       if (tail) {
-        const int r = min(LROWS * rb + l, a.Tq - 1 - q0);
+        const int r = min(16 * w + l, a.Tq - 1 - q0);
         l_off = (unsigned)(r * a.lse.st * 4);
         d_off = (unsigned)(r * a.delta.st * 4);
       }
-      load_lds4(lp + (int64_t)q0 * a.lse.st, l_off, &slse[buf][LROWS * rb]);
-      load_lds4(dp + (int64_t)q0 * a.delta.st, d_off, &sdelta[buf][LROWS * rb]);
+      load_lds4(lp + (int64_t)q0 * a.lse.st, l_off, &slse[buf][16 * w]);
+      load_lds4(dp + (int64_t)q0 * a.delta.st, d_off, &sdelta[buf][16 * w]);
     }
   };
 
@@ -202,22 +191,17 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dk[db] = dv[db] = f32x16{};
 
-  // this share's items qh + QS*j, j < n_j; the larger share has n_jmax
-  const int n_j = n_items > qh ? (n_items - qh + QS - 1) / QS : 0;
-  const int n_jmax = (n_items + QS - 1) / QS;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < n_j) issue_tile(qh + QS * j, j);
+    if (j < n_items) issue_tile(j, j);
 
-  // every query head of the group in turn: dK and dV sum over the group in registers.
-  // Every wave passes one barrier per item of the larger share (a share with fewer pads).
-  for (int j = 0; j < n_j; ++j) {
-    const int it = qh + QS * j;
+  // every query head of the group in turn: dK and dV sum over the group in registers
+  for (int it = 0; it < n_items; ++it) {
     const int t = t_begin + it % n;
-    const int cur = j % NS;
-    wait_tiles<2 * NIQ + 2>(min(NS - 2, n_j - 1 - j));
+    const int cur = it % NS;
+    wait_tiles<2 * C::NI + 2>(min(NS - 2, n_items - 1 - it));
     __syncthreads();
-    if (j + NS - 1 < n_j) issue_tile(qh + QS * (j + NS - 1), (j + NS - 1) % NS);
+    if (it + NS - 1 < n_items) issue_tile(it + NS - 1, (it + NS - 1) % NS);
     const char* Q = sq[cur];
     const char* DO = sdo[cur];
     const int q0 = t * kTile;
@@ -312,8 +296,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     }
   }
 
-  for (int e = n_j; e < n_jmax; ++e) __syncthreads();  // a share with fewer items pads
-
   // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
   if (n_items <= 0 && a.acc) return;
   if constexpr (PART == 0) {
@@ -323,37 +305,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       mfma_agpr_drain(dv[db]);
     }
   }
-  // QS = 2: the odd share stages its dK/dV partials in LDS (same keys, same layout) and
-  // the even share adds them element by element as it stores, so the accumulators are
-  // never copied out of their registers.
-  constexpr int NV = (WANT_DK ? C::NDB * 16 : 0) + (WANT_DV ? C::NDB * 16 : 0);
-  constexpr int DV0 = WANT_DK ? C::NDB * 16 : 0;  // first dV slot of a wave's staging
-  const float* part = nullptr;
-  if constexpr (QS == 2) {
-    static_assert(NR * NV * 64 * 4 <= sizeof(sm), "staging fits the rings");
-    float* cb = (float*)&sm + rb * NV * 64;
-    __syncthreads();  // every wave is done with its rings
-    if (qh == 1) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if constexpr (WANT_DK) cb[(16 * db + r) * 64 + l] = dk[db][r];
-          if constexpr (WANT_DV) cb[(DV0 + 16 * db + r) * 64 + l] = dv[db][r];
-        }
-    }
-    __syncthreads();
-    if (qh == 1) return;
-    part = cb;
-  }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j. The wave's 32
   // rows go through a buffer resource bounded at its last key, so rows past Tk read as zero
   // and drop their stores with no branch. Each accumulator's old values are all read before
   // its first store: the compiler cannot tell dK from dV apart, so read-add-store pairs in
   // turn would each wait for a full memory round trip.
   const int rows = min(32, a.Tk - kw0);
-  auto add_rows = [&](float* base, int64_t st, const f32x16(&acc)[C::NDB], float mul, int slot0)
-                      __attribute__((always_inline)) {
+  auto add_rows = [&](float* base, int64_t st, const f32x16(&acc)[C::NDB], float mul) __attribute__((always_inline)) {
     const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
     // an overwrite reads through an empty range: every read returns 0 and touches no memory
@@ -368,15 +326,13 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = acc[db][r];
-        if constexpr (QS == 2) x += part[(slot0 + 16 * db + r) * 64 + l];
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * x),
-                                              rs, offset(db, r), 0, 0);
-      }
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * acc[db][r]), rs, offset(db, r),
+            0, 0);
   };
-  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale, 0);
-  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f, DV0);
+  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale);
+  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -672,10 +628,10 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   }
 }
 
-template <int D, int NS, int PART, int QS>
+template <int D, int NS, int PART>
 __global__ __launch_bounds__(256, PART == 0 ? 1 : 2) void dkdv_kernel(BwdArgs a, int n_kt) {
-  __shared__ DkdvLds<D, NS, QS> sm;
-  dkdv_body<D, NS, PART, QS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+  __shared__ DkdvLds<D, NS> sm;
+  dkdv_body<D, NS, PART>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
 template <int D, int NS, int KS>
@@ -692,40 +648,19 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
 // are dispatched first, and the short dQ workgroups fill the slots they leave.
 // Workgroups are dealt to the 8 XCDs round-robin by id, so both roles land on
 // every XCD; within a role the ids are remapped as in the single-role kernels.
-template <int D, int NSK, int QSK, int NSQ, int KSQ>
+template <int D, int NSK, int NSQ, int KSQ>
 __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, int n_qt, int n_kv, int n_kv_pad) {
   __shared__ union {
-    DkdvLds<D, NSK, QSK> kv;
+    DkdvLds<D, NSK> kv;
     DqLds<D, NSQ, KSQ> q;
   } sm;
   const int id = blockIdx.x;
   if (id < n_kv_pad) {
     const int L = xcd_remap(id, n_kv_pad);
-    if (L < n_kv) dkdv_body<D, NSK, 0, QSK>(a, L, n_kt, sm.kv);
+    if (L < n_kv) dkdv_body<D, NSK, 0>(a, L, n_kt, sm.kv);
   } else {
     dq_body<D, NSQ, KSQ>(a, xcd_remap(id - n_kv_pad, gridDim.x - n_kv_pad), n_qt, sm.q);
   }
-}
-
-template <int D, int NSK, int QSK, int KSQ>
-void launch_fused(const BwdArgs& a, int n_kt, int nq, int64_t n_kv, int64_t n_dq, hipStream_t s) {
-  const int64_t n_kv_pad = (n_kv + 7) / 8 * 8;
-  hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, QSK, 4, KSQ>), dim3((unsigned)(n_kv_pad + n_dq)), dim3(64 * kNW), 0, s,
-                     a, n_kt, nq, (int)n_kv, (int)n_kv_pad);
-}
-
-// Longest over mean chain of query tiles among the dK/dV workgroups of 128 keys
-// (causal blocks: the first keys are seen by the most rows), as max >= 1.5 mean.
-bool dkdv_imbalanced(const BwdArgs& a, int n_kt) {
-  if (!a.causal) return false;
-  const int t_all = (a.Tq + kTile - 1) / kTile;
-  int64_t mx = 0, sum = 0;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int t = t_all - a.qm.count_lt(a.km.pos(kt * kKeysPerWG)) / kTile;
-    mx = t > mx ? t : mx;
-    sum += t;
-  }
-  return 2 * mx * n_kt >= 3 * sum;
 }
 
 template <int D>
@@ -736,28 +671,21 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;           // (b, query head) for dQ
   const int64_t bkv = (int64_t)a.B * (a.H / a.G);  // (b, KV head) for dK / dV
-  // Under two workgroups per CU, split a dQ workgroup's keys, or a dK/dV workgroup's
-  // query tiles, between two wave pairs (two-stage rings for dK/dV at this width).
-  // The dK/dV split only pays where a few workgroups walk far longer chains than the
-  // rest (a causal diagonal block): it shortens the critical path but adds work that
-  // the dQ workgroups of the shared grid otherwise overlap. The halves called alone
-  // take the same forms, so they equal the shared grid bit for bit.
+  // fewer than two dQ workgroups per CU: split their keys between two wave pairs
   const bool split = D == 64 && bh * n_qt < 512;
-  const bool qsplit = D == 64 && bkv * n_kt < 512 && dkdv_imbalanced(a, n_kt);
   const int n_qt2 = (a.Tq + kQPerWG / 2 - 1) / (kQPerWG / 2);
-  const int n_kt2 = (a.Tk + kKeysPerWG / 2 - 1) / (kKeysPerWG / 2);
   if constexpr (D == 64) {
     // both kernels keep two workgroups per CU at this width, so one grid costs nothing
     if (which == 3) {
-      const int nq = split ? n_qt2 : n_qt, nk = qsplit ? n_kt2 : n_kt;
-      const int64_t n_kv = bkv * nk, n_dq = bh * nq;
-      if (qsplit) {
-        if (split) launch_fused<D, 2, 2, 2>(a, nk, nq, n_kv, n_dq, s);
-        else launch_fused<D, 2, 2, 1>(a, nk, nq, n_kv, n_dq, s);
-      } else {
-        if (split) launch_fused<D, NSK, 1, 2>(a, nk, nq, n_kv, n_dq, s);
-        else launch_fused<D, NSK, 1, 1>(a, nk, nq, n_kv, n_dq, s);
-      }
+      const int nq = split ? n_qt2 : n_qt;
+      const int64_t n_kv = bkv * n_kt, n_kv_pad = (n_kv + 7) / 8 * 8;
+      const int64_t grid = n_kv_pad + bh * nq;
+      if (split)
+        hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 2>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
+                           nq, (int)n_kv, (int)n_kv_pad);
+      else
+        hipLaunchKernelGGL((bwd_fused_kernel<D, NSK, NSQ, 1>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_kt,
+                           nq, (int)n_kv, (int)n_kv_pad);
       return hipGetLastError();
     }
   }
@@ -767,23 +695,17 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     // then dK) that each hold one accumulator and keep two waves per SIMD; S is
     // then formed twice more. Smaller grids (grouped heads) keep one launch:
     // two resident workgroups per CU would leave the heaviest ones as a tail.
-    bool done = false;
+    bool two = false;
     if constexpr (D == 128) {
-      if (bkv * n_kt >= 1024) {
-        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+      two = bkv * n_kt >= 1024;
+      if (two) {
+        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-        done = true;
-      }
-    } else {
-      if (qsplit) {
-        hipLaunchKernelGGL((dkdv_kernel<D, 2, 0, 2>), dim3((unsigned)(bkv * n_kt2)), dim3(64 * kNW), 0, s, a, n_kt2);
-        done = true;
+        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
       }
     }
-    if (!done)
-      hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    if (!two) hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
