@@ -360,7 +360,8 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
 
 def merge_hbm_probe(reps=20):
     """The merge at the 16k-window shape (131072 rows, D=128: 202.9 MB) with the 256 MB
-    last-level cache flushed (512 MB written) before each timed launch."""
+    last-level cache flushed (512 MB written) before each timed launch, next to a device
+    copy (torch ``copy_``) that moves the same number of bytes under the same protocol."""
     import torch
 
     import context_causal_attention_cpattn_amd as cp
@@ -374,21 +375,30 @@ def merge_hbm_probe(reps=20):
     l_blk = torch.randn(B, H, T, device=dev, generator=g)
     flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
     nbytes = B * H * (T - rb) * (12 * D + 12)
-    times = []
-    for i in range(reps + 3):
-        flush.fill_(float(i))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        cp.cpattn_lse_merge(o_acc, l_acc, o_blk, l_blk, rb, T)
-        b.record()
-        torch.cuda.synchronize()
-        if i >= 3:
-            times.append(a.elapsed_time(b))
-    times.sort()
-    med = times[len(times) // 2]
-    return {"rows": B * H * (T - rb), "bytes": nbytes, "median_us": med * 1e3,
-            "GB/s": nbytes / (med / 1e3) / 1e9, "frac_hbm": nbytes / (med / 1e3) / 1e9 / PEAK_HBM_GBS,
-            "note": "512 MB written before each launch to evict the 256 MB last-level cache"}
+    src = torch.ones(nbytes // 8, device=dev)  # read half the bytes, write the other half
+    dst = torch.empty_like(src)
+
+    def median_us(fn):
+        times = []
+        for i in range(reps + 3):
+            flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(a.elapsed_time(b))
+        times.sort()
+        return times[len(times) // 2] * 1e3
+
+    med = median_us(lambda: cp.cpattn_lse_merge(o_acc, l_acc, o_blk, l_blk, rb, T))
+    cop = median_us(lambda: dst.copy_(src))
+    gbs, copy_gbs = nbytes / med / 1e3, nbytes / cop / 1e3
+    return {"rows": B * H * (T - rb), "bytes": nbytes, "median_us": med, "GB/s": gbs,
+            "frac_hbm": gbs / PEAK_HBM_GBS, "copy_GB/s": copy_gbs, "frac_of_copy": gbs / copy_gbs,
+            "note": "512 MB written before each launch to evict the 256 MB last-level cache; the copy "
+                    "moves the same bytes (half read, half written) under the same protocol"}
 
 
 def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):

@@ -16,14 +16,19 @@
 namespace cpattn {
 namespace {
 
+// Each thread owns NV 16-byte slices of one row (D/4/NV threads per row): the two LSE
+// values and the weights are formed once per thread, and the NV loads of each operand
+// are issued together before any arithmetic. Both O operands are read with
+// non-temporal loads (each byte is read once; the result is written in place).
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_vec) {
-  constexpr int VPR = D / 4;  // float4 per row
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_thr) {
+  constexpr int NV = 4;             // float4 per thread
+  constexpr int TPR = D / 4 / NV;   // threads per row
   const int rows = a.row_end - a.row_begin;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec; i += stride) {
-    const int64_t rr = i / VPR;
-    const int c = (int)(i - rr * VPR) * 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_thr; i += stride) {
+    const int64_t rr = i / TPR;
+    const int c = (int)(i - rr * TPR) * 4;  // first column; slices c + 4*TPR*v
     const int64_t bh = rr / rows;
     const int row = a.row_begin + (int)(rr - bh * rows);
     const int b = (int)(bh / a.H), hh = (int)(bh - (int64_t)b * a.H);
@@ -32,23 +37,25 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_vec) 
     const float lav = *la;
     float* oa = a.o_acc + b * a.oa_sb + hh * a.oa_sh + (int64_t)row * a.oa_st + c;
     const float* ob = a.o_blk + b * a.ob_sb + hh * a.ob_sh + (int64_t)row * a.ob_st + c;
-    const f32x4 xa = *(const f32x4*)oa;
-    const f32x4 xb = __builtin_nontemporal_load((const f32x4*)ob);
+    f32x4 xa[NV], xb[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      xa[v] = __builtin_nontemporal_load((const f32x4*)(oa + 4 * TPR * v));
+      xb[v] = __builtin_nontemporal_load((const f32x4*)(ob + 4 * TPR * v));
+    }
     const float m = fmaxf(lav, lb);
-    f32x4 y;
-    float lnew;
-    if (m == -INFINITY) {
-      y = f32x4{0.f, 0.f, 0.f, 0.f};
-      lnew = -INFINITY;
-    } else {
+    float wa = 0.f, wb = 0.f, lnew = -INFINITY;
+    if (m != -INFINITY) {
       const float ea = expf(lav - m), eb = expf(lb - m);  // exp(-inf) = 0
       const float tot = ea + eb;
       const float inv = 1.f / tot;
-      const float wa = ea * inv, wb = eb * inv;
-      y = wa * xa + wb * xb;
+      wa = ea * inv;
+      wb = eb * inv;
       lnew = m + logf(tot);
     }
-    *(f32x4*)oa = y;
+    const bool dead = m == -INFINITY;  // no key seen by the row in either part: O = 0
+#pragma unroll
+    for (int v = 0; v < NV; ++v) *(f32x4*)(oa + 4 * TPR * v) = dead ? f32x4{} : wa * xa[v] + wb * xb[v];
     if (c == 0) *la = lnew;
   }
 }
@@ -56,12 +63,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_vec) 
 template <int D>
 hipError_t merge_d(const MergeArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * (a.row_end - a.row_begin);
-  const int64_t n_vec = rows * (D / 4);
-  if (n_vec <= 0) return hipSuccess;
-  int64_t blocks = (n_vec + 255) / 256;
+  const int64_t n_thr = rows * (D / 16);
+  if (n_thr <= 0) return hipSuccess;
+  int64_t blocks = (n_thr + 255) / 256;
   const int64_t cap = 256 * 64;  // 64 workgroups per CU at most; the loop covers the rest
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, a, n_vec);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)blocks), dim3(256), 0, s, a, n_thr);
   return hipGetLastError();
 }
 
