@@ -436,13 +436,20 @@ GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "b
                "rope_rotate": ("rope_rotate_kernel",), "rope_rotate_grad": ("rope_rotate_grad_kernel",)}
 
 
-def kernel_source_hash():
-    """Hash of every device source of the library: traffic measured on other code is void."""
+TRAFFIC_SOURCES = {"block_bwd": ("bwd_bf16.hip",), "block_bwd_dkdv": ("bwd_bf16.hip",), "block_bwd_dq": ("bwd_bf16.hip",),
+                   "block_fwd": ("fwd_bf16.hip", "fwd_rope_bf16.hip"), "lse_merge": ("merge.hip",),
+                   "bwd_preprocess": ("merge.hip",)}
+
+
+def kernel_source_hash(kernel="block_bwd"):
+    """Hash of the device sources a kernel is built from (its file and the shared headers):
+    traffic measured on other code is void."""
     import hashlib
     d = os.path.join(ROOT, "context_causal_attention_cpattn_amd", "csrc")
+    own = TRAFFIC_SOURCES.get(kernel)
     hsh = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith(".h") or (f.endswith(".hip") and (own is None or f in own)):
             hsh.update(f.encode())
             hsh.update(open(os.path.join(d, f), "rb").read())
     return hsh.hexdigest()[:16]
@@ -483,7 +490,7 @@ def traffic_from(args):
     from workloads import BY_NAME
     w = BY_NAME[args.workload]
     name = "block_bwd" if not args.split_bwd else "block_bwd_dkdv"
-    out = {"kernel": name, "workload": w.name, "source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES,
+    out = {"kernel": name, "workload": w.name, "source_hash": kernel_source_hash(name), "copy_bytes": COPY_BYTES,
            "csv": [os.path.relpath(p, ROOT) for p in args.traffic_from]}
     total = 0.0
     for key, path in zip(("fetch", "write"), args.traffic_from):
@@ -531,7 +538,7 @@ def main():
     traffic = None
     try:
         tj = json.load(open(args.traffic))
-        if tj.get("kernel") == dom and tj.get("workload") == w.name and tj.get("source_hash") == kernel_source_hash():
+        if tj.get("kernel") == dom and tj.get("workload") == w.name and tj.get("source_hash") == kernel_source_hash(dom):
             traffic = tj.get("bytes_per_launch")
     except Exception:
         pass
