@@ -360,8 +360,10 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
 
 def merge_hbm_probe(reps=20):
     """The merge at the 16k-window shape (131072 rows, D=128: 202.9 MB) with the 256 MB
-    last-level cache flushed (512 MB written) before each timed launch, next to a device
-    copy (torch ``copy_``) that moves the same number of bytes under the same protocol."""
+    last-level cache flushed before each timed launch, next to a device copy (torch
+    ``copy_``) that moves the same number of bytes under the same protocol. The flush
+    writes 512 MB and then reads another 512 MB, so the written lines are evicted (and
+    written back) before the timed launch instead of during it."""
     import torch
 
     import context_causal_attention_cpattn_amd as cp
@@ -374,6 +376,7 @@ def merge_hbm_probe(reps=20):
     l_acc = torch.randn(B, H, T, device=dev, generator=g)
     l_blk = torch.randn(B, H, T, device=dev, generator=g)
     flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+    flush_read = torch.ones(512 * 1024 * 1024 // 4, device=dev)
     nbytes = B * H * (T - rb) * (12 * D + 12)
     src = torch.ones(nbytes // 8, device=dev)  # read half the bytes, write the other half
     dst = torch.empty_like(src)
@@ -382,6 +385,8 @@ def merge_hbm_probe(reps=20):
         times = []
         for i in range(reps + 3):
             flush.fill_(float(i))
+            flush_read.sum()
+            torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -397,8 +402,9 @@ def merge_hbm_probe(reps=20):
     gbs, copy_gbs = nbytes / med / 1e3, nbytes / cop / 1e3
     return {"rows": B * H * (T - rb), "bytes": nbytes, "median_us": med, "GB/s": gbs,
             "frac_hbm": gbs / PEAK_HBM_GBS, "copy_GB/s": copy_gbs, "frac_of_copy": gbs / copy_gbs,
-            "note": "512 MB written before each launch to evict the 256 MB last-level cache; the copy "
-                    "moves the same bytes (half read, half written) under the same protocol"}
+            "note": "before each launch 512 MB written, then another 512 MB read, to evict the 256 MB "
+                    "last-level cache; the copy moves the same bytes (half read, half written) under the "
+                    "same protocol"}
 
 
 def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
