@@ -48,8 +48,10 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU clock ramps up over the first tens of milliseconds under load: 200 untimed steps
+    # (about 60 ms at the GPT-2-small shape) let it settle before the 100 timed ones
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="gpt2s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
