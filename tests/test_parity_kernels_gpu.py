@@ -386,6 +386,46 @@ def test_block_bwd_noncausal_ragged():
     assert max(e) <= TOL_BF16
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Tq,Tk,causal", [(1, 1, True), (1, 77, False), (33, 1, True), (130, 3, False), (2, 129, True)])
+def test_block_bwd_tiny_and_degenerate_sizes(Tq, Tk, causal, D):
+    # single rows and single keys, sizes far below one tile and just past it; with causal
+    # maps the keys sit at the positions of the first queries, so every key is seen by the
+    # later rows and the first row sees one key. Both the whole call and the halves.
+    log(f"block_bwd tiny Tq={Tq} Tk={Tk} causal={causal} D={D}")
+    B, H = 2, 3
+    q, do = draw_shape(B, H, Tq, D, torch.bfloat16, seed=181 + Tq, n=2)
+    k, v = draw_shape(B, H, Tk, D, torch.bfloat16, seed=182 + Tk, n=2)
+    qm, km = (Tq, Tq, 0, 0), (Tk, Tk, 0, 0)
+    qp, kp = positions(qm), positions(km)
+    O, L = oa.block_attention_fwd(f64(q), f64(k), f64(v), qp, kp, causal=causal)
+    o = torch.tensor(O, dtype=torch.float32, device=DEV)
+    lse = torch.tensor(L, dtype=torch.float32, device=DEV)
+    delta = torch.empty(B, H, Tq, device=DEV)
+    dod = do.to(DEV)
+    cp.cpattn_bwd_preprocess(dod, o, delta)
+    gq, gk, gv = oa.block_attention_bwd(f64(q), f64(k), f64(v), f64(do), O, L, qp, kp, causal=causal)
+    args = (q.to(DEV), k.to(DEV), v.to(DEV), dod, lse, delta)
+    whole = [torch.zeros(B, H, Tq, D, device=DEV), torch.zeros(B, H, Tk, D, device=DEV),
+             torch.zeros(B, H, Tk, D, device=DEV)]
+    cp.cpattn_block_bwd(*args, *whole, qm, km, causal=causal)
+    halves = [torch.zeros_like(x) for x in whole]
+    cp.cpattn_block_bwd_dkdv(*args, halves[1], halves[2], qm, km, causal=causal)
+    cp.cpattn_block_bwd_dq(*args, halves[0], qm, km, causal=causal)
+    torch.cuda.synchronize()
+    # The kernels round P and dS to bf16 (relative 2^-9) before the fp32-accumulating
+    # products, so the error scales with the output: with three keys a key's dK/dV sums 130
+    # rows at weights near 1/3 and reaches |dV| ~ 20, where the measured error is 0.17 %
+    # (rms, relative) of the reference. The bound is the bf16 tolerance, or 1 % of the
+    # largest reference value where that is larger.
+    for got in (whole, halves):
+        for t, r, name in zip(got, (gq, gk, gv), ("dq", "dk", "dv")):
+            e = max_err(f64(t), r)
+            assert e <= max(TOL_BF16, 1e-2 * float(np.abs(r).max())), (name, e)
+    for a_, b_ in zip(whole, halves):
+        assert torch.equal(a_, b_)
+
+
 def test_bwd_preprocess_fp32_and_bf16():
     log("bwd_preprocess")
     for dtype in (torch.float32, torch.bfloat16):
