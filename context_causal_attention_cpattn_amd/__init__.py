@@ -24,7 +24,8 @@ __all__ = [
     "cpattn_rope_table", "cpattn_rope_rotate", "cpattn_rope_rotate_grad", "cpattn_block_fwd", "cpattn_lse_merge",
     "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
-    "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "EXPORTS",
+    "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
+    "cpattn_ring_bwd", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -36,7 +37,8 @@ EXPORTS = (
     "cpattn_version", "cpattn_last_error", "cpattn_headtail_shard", "cpattn_rope_table", "cpattn_block_fwd",
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
-    "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa",
+    "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
+    "cpattn_ring_bwd",
 )
 
 
@@ -83,6 +85,9 @@ _SIGS = {
                                              _M, _i32, _f32, _i32, _vp]),
     "cpattn_block_bwd_dq": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M, _M,
                                            _i32, _f32, _i32, _vp]),
+    "cpattn_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "cpattn_ring_bwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
+                                       _f32, _T, _T, _T, _T, _T, _T, _i32, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None
@@ -235,6 +240,32 @@ def cpattn_ring_fwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, 
     _check(load().cpattn_ring_fwd(_tensor(q), ks, vs, ms, n, rank, _map(qmap), _dtype(q), B, H, Tq, Tk, D,
                                   int(causal), float(scale), rp, rr, _tensor(o_acc), _tensor(lse_acc, 3), ws, wsb,
                                   _stream(stream)))
+
+
+def cpattn_ring_bwd_workspace_bytes(B: int, H: int, Tq: int) -> int:
+    return int(load().cpattn_ring_bwd_workspace_bytes(B, H, Tq))
+
+
+def cpattn_ring_bwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, dout, o, lse, dq_acc,
+                    dk_blocks: Sequence, dv_blocks: Sequence, workspace, causal: bool = True, scale: float = 0.0,
+                    accumulate: bool = True, stream=None):
+    """Ring backward of rank ``rank``: dq_acc gets the local rows' gradient, dk_blocks[i] / dv_blocks[i] this
+    rank's contribution to block i's."""
+    n = len(k_blocks)
+    if len(v_blocks) != n or len(kmaps) != n or len(dk_blocks) != n or len(dv_blocks) != n:
+        raise ValueError("k_blocks, v_blocks, kmaps, dk_blocks, dv_blocks must have the same length")
+    B, H, Tq, D = q.shape
+    Tk = k_blocks[0].shape[2]
+    ks = (cpattn_tensor * n)(*[_tensor(t) for t in k_blocks])
+    vs = (cpattn_tensor * n)(*[_tensor(t) for t in v_blocks])
+    dks = (cpattn_tensor * n)(*[_tensor(t) for t in dk_blocks])
+    dvs = (cpattn_tensor * n)(*[_tensor(t) for t in dv_blocks])
+    ms = (cpattn_posmap * n)(*[_map(m) for m in kmaps])
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().cpattn_ring_bwd(_tensor(q), ks, vs, ms, n, rank, _map(qmap), _dtype(q), B, H, Tq, Tk, D,
+                                  int(causal), float(scale), _tensor(dout), _tensor(o), _tensor(lse, 3),
+                                  _tensor(dq_acc), dks, dvs, int(accumulate), ws, wsb, _stream(stream)))
 
 
 def cpattn_bwd_preprocess(dout, o, delta, stream=None):

@@ -297,7 +297,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   }
 
   // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
-  if (n_items <= 0 && a.acc) return;
+  if (n_items <= 0 && a.acc_kv) return;
   if constexpr (PART == 0) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -315,7 +315,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
     // an overwrite reads through an empty range: every read returns 0 and touches no memory
-    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, a.acc ? bytes : 0,
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, a.acc_kv ? bytes : 0,
                                                       kBufferFlags);
     auto offset = [&](int db, int r) { return (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db; };
     unsigned old[C::NDB][16];
@@ -384,7 +384,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
   const int n_kt = (n_vis + kKB - 1) / kKB;
   if (n_kt == 0) {  // no key of this block is visible to these rows: nothing to add
-    if (!a.acc && kh == 0 && row_ok) {  // an overwrite writes zeros
+    if (!a.acc_q && kh == 0 && row_ok) {  // an overwrite writes zeros
       float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db)
@@ -609,7 +609,7 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
     float* base = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)w_row0 * a.dq_st;
     const int bytes = wrows > 0 ? ((wrows - 1) * (int)a.dq_st + D) * 4 : 0;  // rows never overlap: st >= D
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kBufferFlags);
-    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, a.acc ? bytes : 0, kBufferFlags);
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, a.acc_q ? bytes : 0, kBufferFlags);
     auto offset = [&](int db, int g) { return (int)((lq * a.dq_st + 32 * db + 8 * g + 4 * h) * 4); };
     u32x4 old[C::NDB][4];
 #pragma unroll

@@ -399,11 +399,13 @@ int cpattn_bwd_preprocess(const cpattn_tensor* dout, int32_t dtype, const cpattn
 
 namespace {
 
-int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, const cpattn_tensor* dout,
-               int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
-               const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq,
-               int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
-               float scale, int32_t accumulate, int which, void* stream, const char* what, int64_t H_kv) {
+// Checks one block backward's arguments and fills its launch arguments; launches nothing.
+// acc_q / acc_kv: 1 adds into dQ / dK and dV, 0 overwrites them.
+int build_bwd(BwdArgs& a, const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+              const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta,
+              const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
+              int64_t H, int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap,
+              int32_t causal, float scale, int32_t acc_q, int32_t acc_kv, int which, int64_t H_kv) {
   int st, G;
   if ((st = check_dims(B, H, Tq, Tk, D))) return st;
   if ((st = group_of(H, H_kv, &G))) return st;
@@ -420,8 +422,9 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
     return fail(CPATTN_EINVAL, "accumulator T stride below D (rows overlap)");
   if ((st = check_map(qmap, Tq, "qmap")) || (st = check_map(kmap, Tk, "kmap"))) return st;
   if (!(scale >= 0.f) || std::isinf(scale)) return fail(CPATTN_EINVAL, "scale must be finite and >= 0");
-  if (accumulate != 0 && accumulate != 1) return fail(CPATTN_EINVAL, "accumulate must be 0 or 1");
-  BwdArgs a{};
+  if (acc_q != 0 && acc_q != 1) return fail(CPATTN_EINVAL, "accumulate must be 0 or 1");
+  if (acc_kv != 0 && acc_kv != 1) return fail(CPATTN_EINVAL, "accumulate must be 0 or 1");
+  a = BwdArgs{};
   a.q = view(q), a.k = view(k), a.v = view(v), a.dout = view(dout);
   a.lse = view(lse), a.delta = view(delta);
   if (which & 2) a.dq = (float*)dq_acc->data, a.dq_sb = dq_acc->sb, a.dq_sh = dq_acc->sh, a.dq_st = dq_acc->st;
@@ -434,7 +437,20 @@ int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tens
   a.causal = causal != 0;
   a.scale = scale == 0.f ? (float)(1.0 / std::sqrt((double)D)) : scale;
   a.G = G;
-  a.acc = accumulate;
+  a.acc_q = acc_q;
+  a.acc_kv = acc_kv;
+  return ok();
+}
+
+int bwd_common(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, const cpattn_tensor* dout,
+               int32_t dtype, const cpattn_tensor* lse, const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
+               const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t Tq,
+               int64_t Tk, int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+               float scale, int32_t accumulate, int which, void* stream, const char* what, int64_t H_kv) {
+  BwdArgs a;
+  int st = build_bwd(a, q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap,
+                     causal, scale, accumulate, accumulate, which, H_kv);
+  if (st) return st;
   return launch_status(launch_bwd_bf16(a, which, (hipStream_t)stream), what);
 }
 
@@ -479,6 +495,54 @@ int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cp
                         int32_t accumulate, void* stream) {
   return bwd_common(q, k, v, dout, dtype, lse, delta, dq_acc, nullptr, nullptr, B, H, Tq, Tk, D, qmap, kmap, causal,
                     scale, accumulate, 2, stream, "block_bwd_dq", H);
+}
+
+// Workspace layout: [fp32 delta, B x H x Tq], 256-byte aligned.
+size_t cpattn_ring_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq) {
+  if (B <= 0 || H <= 0 || Tq <= 0) return 0;
+  return ws_part((size_t)B * H * Tq * 4);
+}
+
+int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const cpattn_tensor* v_blocks,
+                    const cpattn_posmap* kmaps, int32_t ring, int32_t rank, const cpattn_posmap* qmap,
+                    int32_t dtype, int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t causal,
+                    float scale, const cpattn_tensor* dout, const cpattn_tensor* o, const cpattn_tensor* lse,
+                    const cpattn_tensor* dq_acc, const cpattn_tensor* dk_blocks, const cpattn_tensor* dv_blocks,
+                    int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream) {
+  if (ring < 1) return fail(CPATTN_EINVAL, "ring must be >= 1");
+  if (rank < 0 || rank >= ring) return fail(CPATTN_EINVAL, "rank outside [0, ring)");
+  if (!k_blocks || !v_blocks || !kmaps || !dk_blocks || !dv_blocks) return fail(CPATTN_EINVAL, "null block arrays");
+  int st;
+  if ((st = check_dims(B, H, Tq, Tk, D))) return st;
+  if ((st = check_tensor(o, "o", 4))) return st;
+  const size_t need = cpattn_ring_bwd_workspace_bytes(B, H, Tq);
+  if (!workspace || workspace_bytes < need) return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");
+  const cpattn_tensor delta{workspace, H * Tq, Tq, 1};
+  // validate every step before launching anything
+  for (int32_t i = 0; i < ring; ++i) {
+    BwdArgs a;
+    if ((st = build_bwd(a, q, &k_blocks[i], &v_blocks[i], dout, dtype, lse, &delta, dq_acc, &dk_blocks[i],
+                        &dv_blocks[i], B, H, Tq, Tk, D, qmap, &kmaps[i], causal, scale, 1, accumulate, 3, H)))
+      return st;
+  }
+  if ((st = cpattn_bwd_preprocess(dout, dtype, o, &delta, B, H, Tq, D, stream))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  for (int32_t step = 0; step < ring; ++step) {
+    const int32_t src = ((rank - step) % ring + ring) % ring;
+    int64_t rb = 0, nvis = 0;
+    if ((st = cpattn_step_rows(qmap, &kmaps[src], causal, &rb, &nvis))) return st;
+    // dQ takes every step's contribution: only the first step may overwrite it
+    const int32_t acc_q = (accumulate || step > 0) ? 1 : 0;
+    // no local row sees this block and nothing has to be overwritten: no work
+    if (rb >= Tq && acc_q && accumulate) continue;
+    BwdArgs a;
+    build_bwd(a, q, &k_blocks[src], &v_blocks[src], dout, dtype, lse, &delta, dq_acc, &dk_blocks[src],
+              &dv_blocks[src], B, H, Tq, Tk, D, qmap, &kmaps[src], causal, scale, acc_q, accumulate, 3, H);
+    hipError_t e = launch_bwd_bf16(a, 3, s);
+    if (e != hipSuccess) return launch_status(e, "ring_bwd block");
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -65,7 +65,9 @@ struct BwdArgs {
   int causal;
   float scale;
   int G;  // query heads per KV head; dK / dV are per KV head, summed over its group
-  int acc;  // 1: add into the accumulators; 0: overwrite them (zeros where no pair contributes)
+  // 1: add into the accumulator; 0: overwrite it (zeros where no pair contributes)
+  int acc_q;   // dQ
+  int acc_kv;  // dK and dV
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

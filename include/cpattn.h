@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 3
+#define CPATTN_ABI_VERSION 4
 
 enum {
   CPATTN_OK = 0,
@@ -319,6 +319,45 @@ int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cp
                         int64_t Tq, int64_t Tk, int64_t D, const cpattn_posmap* qmap,
                         const cpattn_posmap* kmap, int32_t causal, float scale, int32_t accumulate,
                         void* stream);
+
+/* Workspace bytes cpattn_ring_bwd needs: the fp32 delta of the local rows. 0 for non-positive sizes. */
+size_t cpattn_ring_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq);
+
+/*
+ * Ring backward of rank `rank` out of `ring`, all KV blocks resident in HBM:
+ * the backward of cpattn_ring_fwd. It runs cpattn_bwd_preprocess into the
+ * workspace, then one cpattn_block_bwd per step in the forward's order (step s
+ * uses the block of owner (rank - s) mod ring), each with the final o and lse
+ * of the local rows: every step rebuilds its P from the final LSE, which in
+ * exact arithmetic equals the per-step saved (O, LSE) with the merge
+ * rescaling of the backward (BluScriptCP log, 2026-03-21, the backward merger
+ * fix), so no per-step statistics are kept.
+ * dq_acc [B,H,Tq,D] fp32 gathers every step's contribution; dk_blocks[i] and
+ * dv_blocks[i] [B,H,Tk,D] fp32 get this rank's contribution to block i's
+ * gradient (in a real ring that partial travels back to rank i and is summed
+ * there with the other ranks' partials).
+ * accumulate = 1 adds everything into the accumulators. accumulate = 0
+ * overwrites: dq_acc takes the first step's contribution (every row written)
+ * and adds the rest; each dk/dv block is written in full by its own step.
+ * Steps whose block no local row sees are skipped when accumulate = 1.
+ * q, k_blocks, v_blocks, dout bf16 (rotary is not applied here: pass the
+ * rotated Q and K blocks that the forward used, then map dq and the dk blocks
+ * back with cpattn_rope_rotate_grad); o and lse are cpattn_ring_fwd's outputs.
+ * Multi-head only (H_kv = H). ring + 1 launches at most, no synchronisation.
+ * workspace: device memory of cpattn_ring_bwd_workspace_bytes(B,H,Tq) bytes,
+ * 256-byte aligned.
+ * Errors: as cpattn_block_bwd for any step (checked before any launch), plus
+ * EINVAL for ring < 1, rank out of range, null block arrays, a short or
+ * misaligned workspace.
+ */
+int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks,
+                    const cpattn_tensor* v_blocks, const cpattn_posmap* kmaps,
+                    int32_t ring, int32_t rank, const cpattn_posmap* qmap, int32_t dtype,
+                    int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t causal,
+                    float scale, const cpattn_tensor* dout, const cpattn_tensor* o,
+                    const cpattn_tensor* lse, const cpattn_tensor* dq_acc,
+                    const cpattn_tensor* dk_blocks, const cpattn_tensor* dv_blocks,
+                    int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

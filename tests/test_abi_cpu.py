@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 3
+    assert cp.cpattn_version() == 4
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -112,6 +112,40 @@ def test_ring_fwd_rejects():
     assert lib.cpattn_ring_fwd(*args(2, 0, None, 0)) == -1  # no workspace
     assert lib.cpattn_ring_fwd(*args(2, 0, ctypes.c_void_p(0x100010), 1 << 20)) == -1  # misaligned workspace
     assert "workspace" in cp.cpattn_last_error()
+
+
+def test_ring_bwd_rejects_before_any_launch():
+    lib = cp.load()
+    n = 2
+    ks = (cp.cpattn_tensor * n)(_t(), _t())
+    good_maps = (cp.cpattn_posmap * n)(cp.cpattn_posmap(64, 32, 0, 64), cp.cpattn_posmap(64, 32, 32, 32))
+    qm = cp.cpattn_posmap(64, 32, 0, 64)
+    o, lse = _t(), _t(st=1)
+    ws_ok = ctypes.c_void_p(0x100000)
+
+    def call(ring=2, rank=0, ws=ws_ok, wsb=1 << 20, dtype=1, acc=1, maps=good_maps, dks=ks):
+        return lib.cpattn_ring_bwd(ctypes.byref(_t()), ks, ks, maps, ring, rank, ctypes.byref(qm), dtype, 1, 1, 64,
+                                   64, 64, 1, 0.0, ctypes.byref(_t()), ctypes.byref(o), ctypes.byref(lse),
+                                   ctypes.byref(_t()), dks, ks, acc, ws, wsb, None)
+
+    assert call(ring=0) == -1
+    assert call(rank=2) == -1
+    assert call(ws=None, wsb=0) == -1 and "workspace" in cp.cpattn_last_error()
+    assert call(wsb=255) == -1 and "workspace" in cp.cpattn_last_error()  # 64 fp32 deltas need 256 bytes
+    assert call(ws=ctypes.c_void_p(0x100010)) == -1 and "aligned" in cp.cpattn_last_error()
+    assert call(dtype=0) == -2  # fp32 backward
+    assert call(acc=2) == -1 and "accumulate" in cp.cpattn_last_error()
+    # an invalid map or accumulator of the LAST step is found before the first step launches
+    bad_maps = (cp.cpattn_posmap * n)(cp.cpattn_posmap(64, 32, 0, 64), cp.cpattn_posmap(64, 70, 0, 0))
+    assert call(maps=bad_maps) == -1
+    overlap = (cp.cpattn_tensor * n)(_t(), _t(st=32))
+    assert call(dks=overlap) == -1 and "overlap" in cp.cpattn_last_error()
+
+
+def test_ring_bwd_workspace_size():
+    assert cp.cpattn_ring_bwd_workspace_bytes(1, 16, 16384) == 16 * 16384 * 4
+    assert cp.cpattn_ring_bwd_workspace_bytes(1, 1, 3) == 256
+    assert cp.cpattn_ring_bwd_workspace_bytes(0, 1, 1) == 0
 
 
 def test_ring_workspace_size():

@@ -45,11 +45,11 @@ class Share:
         cp.cpattn_ring_fwd(self.q, self.kb, self.vb, self.maps, self.rank, self.maps[self.rank], self.o, self.lse,
                            self.ws, rope_table=self.tab)
 
-    def backward(self, dk, dv):
+    def backward(self, dk, dv, dq=None):
         w, N, r = self.w, self.w.ring, self.rank
         self.delta = torch.empty(w.B, w.H, w.local_len, device=DEV)
         cp.cpattn_bwd_preprocess(self.do, self.o, self.delta)
-        self.dq = torch.zeros_like(self.o)
+        self.dq = torch.zeros_like(self.o) if dq is None else dq
         for s in range(N):
             src = (r - s) % N
             cp.cpattn_block_bwd(self.q, self.kb[src], self.vb[src], self.do, self.lse, self.delta, self.dq, dk[src],
@@ -232,3 +232,94 @@ def test_win32k_rope_backward_all_ranks_sampled():
     rv = float((np.abs(vsum - dosum) / np.abs(vglob).sum(axis=2)).max())
     log(f"  invariants: |sum R dK| / sum|dK| {rk:.3g}, |sum dV - sum dO| / sum|dV| {rv:.3g}")
     assert rk <= 1e-3 and rv <= 1e-3
+
+
+def _ring_bwd(s, dq, dk, dv, accumulate):
+    w = s.w
+    ws = torch.empty(cp.cpattn_ring_bwd_workspace_bytes(w.B, w.H, w.local_len), dtype=torch.uint8, device=DEV)
+    cp.cpattn_ring_bwd(s.q, s.kb, s.vb, s.maps, s.rank, s.maps[s.rank], s.do, s.o, s.lse, dq, dk, dv, ws,
+                       accumulate=accumulate)
+
+
+@pytest.mark.parametrize("name,rank", [("gpt2s", 1), ("bwd16k", 1)])
+def test_ring_bwd_equals_step_driven_backward(name, rank):
+    """The one-call ring backward launches the same kernels as the per-step calls: overwriting
+    NaN-filled accumulators gives exactly the per-step result into zeros, and adding into filled
+    accumulators gives exactly the per-step result from the same fill."""
+    w = BY_NAME[name]
+    log(f"workload {w.name} rank {rank}")
+    t = draw(w)
+    if "do" not in t:
+        g = torch.Generator().manual_seed(w.seed + 1000)
+        t["do"] = torch.randn(w.B, w.H, w.T, w.D, generator=g).to(torch.bfloat16)
+    s = Share(w, t, rank)
+    s.forward()
+    shape = (w.B, w.H, w.local_len, w.D)
+    dk_ref = [torch.zeros(shape, device=DEV) for _ in range(w.ring)]
+    dv_ref = [torch.zeros(shape, device=DEV) for _ in range(w.ring)]
+    s.backward(dk_ref, dv_ref)
+    nan = lambda: torch.full(shape, float("nan"), device=DEV)
+    dq, dk, dv = nan(), [nan() for _ in range(w.ring)], [nan() for _ in range(w.ring)]
+    _ring_bwd(s, dq, dk, dv, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, s.dq)
+    for i in range(w.ring):
+        assert torch.equal(dk[i], dk_ref[i]) and torch.equal(dv[i], dv_ref[i]), i
+    # accumulate: both forms start from the same fill
+    g = torch.Generator(device="cpu").manual_seed(7)
+    fill = [torch.randn(shape, generator=g).to(DEV) for _ in range(1 + 2 * w.ring)]
+    dq2, dk2, dv2 = fill[0].clone(), [x.clone() for x in fill[1:1 + w.ring]], [x.clone() for x in fill[1 + w.ring:]]
+    _ring_bwd(s, dq2, dk2, dv2, accumulate=True)
+    dk_ref2, dv_ref2 = [x.clone() for x in fill[1:1 + w.ring]], [x.clone() for x in fill[1 + w.ring:]]
+    s.backward(dk_ref2, dv_ref2, dq=fill[0].clone())
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, s.dq)
+    for i in range(w.ring):
+        assert torch.equal(dk2[i], dk_ref2[i]) and torch.equal(dv2[i], dv_ref2[i]), i
+    log(f"  ring backward equals the per-step calls ({w.ring} steps)")
+
+
+def test_ring_bwd_contiguous_shards_with_invisible_blocks():
+    """Contiguous sharding (rank r holds [r L, (r+1) L)): every later rank's block lies in the future
+    of all local rows. Overwriting writes zeros for those blocks, adding leaves them untouched,
+    and the visible blocks match the oracle."""
+    from workloads import Workload
+    w = Workload("contig", 11, B=1, H=2, D=64, T=1024, ring=4, dtype="bf16", backward=True)
+    t = draw(w)
+    t64 = {n: f64(x) for n, x in t.items()}
+    L = w.T // w.ring
+    maps = [cp.cpattn_posmap(L, L, r * L, r * L) for r in range(w.ring)]
+    pos = [list(range(r * L, (r + 1) * L)) for r in range(w.ring)]
+    kb = [gather(t["k"], p) for p in pos]
+    vb = [gather(t["v"], p) for p in pos]
+    shape = (w.B, w.H, L, w.D)
+    for rank in (0, 2):
+        log(f"  contiguous rank {rank}")
+        q, do = gather(t["q"], pos[rank]), gather(t["do"], pos[rank])
+        o = torch.empty(shape, device=DEV)
+        lse = torch.empty(w.B, w.H, L, device=DEV)
+        wsf = torch.empty(cp.cpattn_ring_fwd_workspace_bytes(w.B, w.H, L, w.D), dtype=torch.uint8, device=DEV)
+        cp.cpattn_ring_fwd(q, kb, vb, maps, rank, maps[rank], o, lse, wsf)
+        ws = torch.empty(cp.cpattn_ring_bwd_workspace_bytes(w.B, w.H, L), dtype=torch.uint8, device=DEV)
+        nan = lambda: torch.full(shape, float("nan"), device=DEV)
+        dq, dk, dv = nan(), [nan() for _ in range(w.ring)], [nan() for _ in range(w.ring)]
+        cp.cpattn_ring_bwd(q, kb, vb, maps, rank, maps[rank], do, o, lse, dq, dk, dv, ws, accumulate=False)
+        fill = [torch.full(shape, 3.0, device=DEV) for _ in range(2 * w.ring)]
+        dk2, dv2 = fill[:w.ring], fill[w.ring:]
+        dq2 = torch.zeros(shape, device=DEV)
+        cp.cpattn_ring_bwd(q, kb, vb, maps, rank, maps[rank], do, o, lse, dq2, dk2, dv2, ws, accumulate=True)
+        torch.cuda.synchronize()
+        rows = pos[rank]
+        O, Lr = oa.causal_attention_fwd(t64["q"], t64["k"], t64["v"], rows=rows)
+        gq, gk, gv = oa.block_attention_bwd(t64["q"][:, :, rows], t64["k"], t64["v"], t64["do"][:, :, rows], O, Lr,
+                                            rows, np.arange(w.T))
+        errs = [max_err(f64(dq), gq), max_err(f64(dq2), gq)]
+        for src in range(w.ring):
+            p = pos[src]
+            if src > rank:  # invisible: zeros when overwriting, untouched when adding
+                assert torch.count_nonzero(dk[src]) == 0 and torch.count_nonzero(dv[src]) == 0
+                assert bool((dk2[src] == 3.0).all()) and bool((dv2[src] == 3.0).all())
+            errs += [max_err(f64(dk[src]), gk[:, :, p]), max_err(f64(dv[src]), gv[:, :, p]),
+                     max_err(f64(dk2[src]) - 3.0, gk[:, :, p]), max_err(f64(dv2[src]) - 3.0, gv[:, :, p])]
+        log(f"  rank {rank}: max err {max(errs):.3g}")
+        assert max(errs) <= TOL_BF16
