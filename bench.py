@@ -60,6 +60,8 @@ def parse():
                     help="counter-collection run: eager steps, then the calibration copy")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from two rocprofv3 counter-collection CSVs")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="run the LSE merge as its own launch after each block forward (two-launch form)")
     ap.add_argument("--split-bwd", action="store_true",
                     help="call the two halves of the block backward separately (per-half timings)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -129,6 +131,9 @@ class Share:
         self.bh = w.B * w.H
 
     split_bwd = False
+    # ring steps after the first fold their rows into the running (O, LSE) in the block
+    # kernel's epilogue (cpattn_block_fwd_merge); False: block output, then cpattn_lse_merge
+    fused_merge = True
 
     def build_plan(self, do_bwd=True):
         """Marshal every launch of one step once: (name, work, fn, args). The calls are the
@@ -169,6 +174,11 @@ class Share:
                 plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
                              (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
                 k = kr
+            if s > 0 and self.fused_merge:
+                plan.append(("block_fwd_merge", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_merge,
+                             (by(qf), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, rb, Tl,
+                              by(o), by(lse), st)))
+                continue
             oo, ll = (o, lse) if s == 0 else (ob, lb)
             if gqa:
                 plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_gqa,
@@ -264,7 +274,7 @@ class _no_event:
 class EventLog:
     """HIP events around each launch on torch's current stream (the library's stream)."""
 
-    BOUND = {"block_fwd": "mfma", "block_bwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma",
+    BOUND = {"block_fwd": "mfma", "block_fwd_merge": "mfma", "block_bwd": "mfma", "block_bwd_dkdv": "mfma", "block_bwd_dq": "mfma",
              "lse_merge": "hbm", "bwd_preprocess": "hbm", "rope_rotate": "hbm", "rope_rotate_grad": "hbm"}
 
     def __init__(self):
@@ -445,7 +455,8 @@ GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "b
 
 
 TRAFFIC_SOURCES = {"block_bwd": ("bwd_bf16.hip",), "block_bwd_dkdv": ("bwd_bf16.hip",), "block_bwd_dq": ("bwd_bf16.hip",),
-                   "block_fwd": ("fwd_bf16.hip", "fwd_rope_bf16.hip"), "lse_merge": ("merge.hip",),
+                   "block_fwd": ("fwd_bf16.hip", "fwd_rope_bf16.hip"), "block_fwd_merge": ("fwd_bf16.hip",),
+                   "lse_merge": ("merge.hip",),
                    "bwd_preprocess": ("merge.hip",)}
 
 
@@ -470,6 +481,7 @@ def pmc_run(args):
     w = BY_NAME[args.workload]
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
+    share.fused_merge = not args.separate_merge
     share.build_plan(True)
     for _ in range(3):
         share.step()
@@ -538,6 +550,7 @@ def main():
     w = BY_NAME[args.workload]
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
+    share.fused_merge = not args.separate_merge
     wall, kern, graphed = time_steps(share, args.steps, args.warmup, graph=not args.no_graph)
     flops = share.flops()
     value = flops / wall / 1e12
@@ -565,7 +578,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: rank 0 share of causal ring attention, HeadTail, B={w.B} H={w.H} "
-                               f"D={w.D} T={w.T} ring={w.ring}, forward (block fwd + LSE merge) and backward "
+                               f"D={w.D} T={w.T} ring={w.ring}, forward (block fwd; LSE merge in the block kernel's "
+                               f"epilogue from step 1 on) and backward "
                                f"(preprocess + dK/dV + dQ), all KV blocks resident",
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "ring": w.ring, "rank": 0,
                    "causal_pairs_per_head": share.pairs, "flops_per_step": flops,
@@ -593,6 +607,19 @@ def main():
                                            "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
             del sx
             torch.cuda.empty_cache()
+        # the 16k window forward with the merge as its own launch (the two-launch form)
+        wx = BY_NAME["win16k"]
+        sx = Share(wx, seed_do=wx.seed + 1000)
+        sx.fused_merge = False
+        wl, kx, _ = time_steps(sx, 3, 1, do_bwd=False)
+        fl = sx.flops(False)
+        extra["win16k_fwd_two_launch_merge"] = {
+            "ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
+            "parts": "forward only, block output then cpattn_lse_merge",
+            "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
+                            "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
+        del sx
+        torch.cuda.empty_cache()
         extra["merge_hbm_16k"] = merge_hbm_probe()
         line["other_workloads"] = extra
     if not args.no_cpu_baseline:

@@ -25,7 +25,7 @@ __all__ = [
     "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
     "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
-    "cpattn_ring_bwd", "EXPORTS",
+    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +38,7 @@ EXPORTS = (
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
     "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
-    "cpattn_ring_bwd",
+    "cpattn_ring_bwd", "cpattn_block_fwd_merge",
 )
 
 
@@ -85,6 +85,8 @@ _SIGS = {
                                              _M, _i32, _f32, _i32, _vp]),
     "cpattn_block_bwd_dq": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _i64, _i64, _i64, _i64, _i64, _M, _M,
                                            _i32, _f32, _i32, _vp]),
+    "cpattn_block_fwd_merge": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32,
+                                              _f32, _i64, _i64, _T, _T, _vp]),
     "cpattn_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "cpattn_ring_bwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _T, _T, _T, _T, _T, _T, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -313,6 +315,18 @@ def cpattn_block_fwd_gqa(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale
     _check(load().cpattn_block_fwd_gqa(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
                                        _map(qmap), _map(kmap), int(causal), float(scale), rp, rr, row_begin, row_end,
                                        _tensor(o), _tensor(lse, 3), _stream(stream)))
+
+
+def cpattn_block_fwd_merge(q, k, v, qmap, kmap, o_acc, lse_acc, causal: bool = True, scale: float = 0.0,
+                           row_begin: int = 0, row_end: int | None = None, stream=None):
+    """Block forward of rows [row_begin, row_end) folded into the running (o_acc, lse_acc) in one launch
+    (k / v may have fewer heads than q: grouped-query)."""
+    B, H, Tq, D = q.shape
+    H_kv, Tk = k.shape[1], k.shape[2]
+    row_end = Tq if row_end is None else row_end
+    _check(load().cpattn_block_fwd_merge(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
+                                         _map(qmap), _map(kmap), int(causal), float(scale), row_begin, row_end,
+                                         _tensor(o_acc), _tensor(lse_acc, 3), _stream(stream)))
 
 
 def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,

@@ -243,6 +243,22 @@ int cpattn_block_fwd_gqa(const cpattn_tensor* q, const cpattn_tensor* k, const c
   return launch_status(dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s), "block_fwd_gqa");
 }
 
+int cpattn_block_fwd_merge(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
+                           const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
+                           int64_t row_begin, int64_t row_end, const cpattn_tensor* o_acc,
+                           const cpattn_tensor* lse_acc, void* stream) {
+  FwdArgs a{};
+  int G;
+  int st = build_fwd(a, q, k, v, dtype, B, H, Tq, Tk, D, qmap, kmap, causal, scale, nullptr, 0, row_begin, row_end,
+                     o_acc, lse_acc);
+  if (st || (st = group_of(H, H_kv, &G))) return st;
+  if (dtype != CPATTN_BF16) return fail(CPATTN_EUNSUPPORTED, "block_fwd_merge takes bf16 inputs");
+  a.G = G;
+  a.merge = 1;
+  return launch_status(launch_fwd_bf16(a, (hipStream_t)stream), "block_fwd_merge");
+}
+
 int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, const cpattn_tensor* o_blk,
                      const cpattn_tensor* lse_blk, int64_t B, int64_t H, int64_t T, int64_t D, int64_t row_begin,
                      int64_t row_end, void* stream) {
@@ -360,6 +376,17 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
     if (rb >= Tq) continue;  // the whole block is in the future of every local row
     const cpattn_tensor* kb = key_block(src);
     if (!kb) return CPATTN_EHIP;
+    if (dtype == CPATTN_BF16 && blk_rope == nullptr) {
+      // bf16 without per-tile rotary: the block kernel merges its rows into the accumulator
+      // in its epilogue (no block output in the workspace, no merge launch)
+      FwdArgs a{};
+      build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, nullptr, 0, rb, Tq,
+                o_acc, lse_acc);
+      a.merge = 1;
+      hipError_t e = launch_fwd_bf16(a, s);
+      if (e != hipSuccess) return launch_status(e, "ring_fwd block merge");
+      continue;
+    }
     FwdArgs a{};
     build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, blk_rope, rope_rows, rb, Tq,
               &o_blk, &l_blk);

@@ -421,24 +421,56 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
     m_run = mm;
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2; with a.merge the row is folded into
+  // the running (O, LSE) instead, with the arithmetic of the merge kernel (merge.hip)
   const float l_tot = l_part + __shfl_xor(l_part, 32);
   if (row_ok) {
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
+    const float lb = live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     float* op = a.o + b * a.o_sb + hh * a.o_sh + (int64_t)row * a.o_st;
+    float* lp = a.lse + b * a.l_sb + hh * a.l_sh + (int64_t)row * a.l_st;
+    if (a.merge) {
+      // both lanes of the row read the running LSE and their half of the running O before
+      // any store
+      const float lav = *lp;
+      f32x4 xa[C::NDB][4];
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db)
+      for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v4[j] = acc[db][4 * g + j] * inv;
-        *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = v4;
+        for (int g = 0; g < 4; ++g) xa[db][g] = *(const f32x4*)(op + 32 * db + 8 * g + 4 * h);
+      const float m = fmaxf(lav, lb);
+      float wa = 0.f, wb = 0.f, lnew = -INFINITY;
+      if (m != -INFINITY) {
+        const float ea = expf(lav - m), eb = expf(lb - m);
+        const float tot = ea + eb;
+        const float r = 1.f / tot;
+        wa = ea * r;
+        wb = eb * r;
+        lnew = m + logf(tot);
       }
-    if (h == 0) {
-      a.lse[b * a.l_sb + hh * a.l_sh + (int64_t)row * a.l_st] =
-          live ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+      const bool dead = m == -INFINITY;  // no key seen in either part: O = 0
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 ob;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ob[j] = acc[db][4 * g + j] * inv;
+          *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = dead ? f32x4{} : wa * xa[db][g] + wb * ob;
+        }
+      if (h == 0) *lp = lnew;
+    } else {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = acc[db][4 * g + j] * inv;
+          *(f32x4*)(op + 32 * db + 8 * g + 4 * h) = v4;
+        }
+      if (h == 0) *lp = lb;
     }
   }
 }

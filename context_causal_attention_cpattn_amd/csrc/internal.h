@@ -27,6 +27,7 @@ struct FwdArgs {
   int rope_rows;
   int row_begin, row_end;
   int G;  // query heads per KV head: query head h reads K and V head h / G
+  int merge;  // 1: fold the block result into (o, lse) as the log-sum-exp merge does; 0: write it
 };
 
 struct MergeArgs {

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 4
+#define CPATTN_ABI_VERSION 5
 
 enum {
   CPATTN_OK = 0,
@@ -189,6 +189,26 @@ int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc,
                      int64_t row_begin, int64_t row_end, void* stream);
 
 /*
+ * Block forward fused with the log-sum-exp merge: the result of
+ * cpattn_block_fwd_gqa on rows [row_begin, row_end) (H_kv = H for multi-head)
+ * is folded into the running fp32 (o_acc, lse_acc) in the kernel's epilogue,
+ * with the arithmetic of cpattn_lse_merge (SDPAMerger of the BluScriptCP log,
+ * 2026-03-20; partial-row merge, 2026-05-20), instead of being written out
+ * and merged by a second launch. Same result as cpattn_block_fwd into a
+ * scratch pair followed by cpattn_lse_merge, up to rounding order; it moves
+ * about half the bytes (no block output is written and read back) and saves
+ * one launch per ring step. Rows outside the range are untouched. A row that
+ * sees no key of this block and none before keeps O = 0, LSE = -inf.
+ * bf16 inputs only, no rotary table (pass rotated Q and K: cpattn_rope_rotate).
+ * Errors: as cpattn_block_fwd_gqa; EUNSUPPORTED for fp32 inputs.
+ */
+int cpattn_block_fwd_merge(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                           int32_t dtype, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                           int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap,
+                           int32_t causal, float scale, int64_t row_begin, int64_t row_end,
+                           const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, void* stream);
+
+/*
  * Step classification (host only, integer, exact): the local query rows that
  * see at least one key of a KV block. Positions increase with the local
  * index, so they form the suffix [*row_begin, qmap->len); *visible_keys is the
@@ -219,9 +239,11 @@ size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t
  * (each [B,H,Tk,D]). At step s the rank holds the block of owner
  * (rank - s) mod ring (blocks travel to the next rank each step). Step 0
  * writes (o_acc, lse_acc) directly; every later step runs the block forward
- * on the rows that see at least one key of that block, into the workspace,
- * then merges those rows. Steps whose block is invisible to every row are
- * skipped. At most two launches per step, no synchronisation. With a rotary
+ * on the rows that see at least one key of that block and merges those rows:
+ * with bf16 inputs in the block kernel's epilogue (cpattn_block_fwd_merge, one
+ * launch), with fp32 inputs into the workspace and then by cpattn_lse_merge.
+ * Steps whose block is invisible to every row are skipped. At most two
+ * launches per step, no synchronisation. With a rotary
  * table and bf16 inputs, Q is rotated once (cpattn_rope_rotate) and each step
  * first rotates its K block into the workspace, then runs the block without
  * rotation (one more launch per step).

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 4
+    assert cp.cpattn_version() == 5
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -146,6 +146,19 @@ def test_ring_bwd_workspace_size():
     assert cp.cpattn_ring_bwd_workspace_bytes(1, 16, 16384) == 16 * 16384 * 4
     assert cp.cpattn_ring_bwd_workspace_bytes(1, 1, 3) == 256
     assert cp.cpattn_ring_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def test_block_fwd_merge_rejects_before_launch():
+    lib = cp.load()
+    m = cp.cpattn_posmap(64, 64, 0, 0)
+    t, l3 = _t(), _t(st=1)
+    bt, bm, bl = ctypes.byref(t), ctypes.byref(m), ctypes.byref(l3)
+    call = lambda dtype=1, H=2, H_kv=2, rb=0, re=64, D=64: lib.cpattn_block_fwd_merge(
+        bt, bt, bt, dtype, 1, H, H_kv, 64, 64, D, bm, bm, 1, 0.0, rb, re, bt, bl, None)
+    assert call(dtype=0) == -2 and "bf16" in cp.cpattn_last_error()  # fp32 inputs
+    assert call(H=4, H_kv=3) == -1                                    # not a group
+    assert call(rb=10, re=10) == -1                                   # empty row range
+    assert call(D=96) == -2
 
 
 def test_ring_workspace_size():

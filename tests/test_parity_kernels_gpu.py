@@ -63,6 +63,57 @@ def test_lse_merge(D, rb, re):
 
 # ----------------------------------------------------------------------------- block forward
 
+MERGE_FUSED_CASES = [
+    # B, H, H_kv, Tq, Tk, D, qmap, kmap, rows
+    (1, 2, 2, 300, 200, 128, (300, 150, 1000, 1300), (200, 100, 900, 1200), (0, 300)),
+    (2, 3, 3, 257, 190, 64, (257, 128, 300, 700), (190, 95, 100, 800), (61, 257)),   # row range, small grid
+    (2, 32, 32, 1024, 512, 64, (1024, 512, 0, 1536), (512, 256, 256, 1280), (0, 1024)),  # large grid at D = 64
+    (1, 4, 2, 200, 260, 128, (200, 100, 0, 700), (260, 130, 50, 600), (0, 200)),     # grouped-query
+    (1, 2, 2, 128, 128, 128, (128, 128, 0, 0), (128, 128, 1000, 1000), (0, 128)),    # block invisible to all
+]
+
+
+@pytest.mark.parametrize("case", range(len(MERGE_FUSED_CASES)))
+def test_block_fwd_merge_matches_fwd_then_merge(case):
+    """One launch that folds its rows into the running (O, LSE) equals the block forward followed by
+    the merge kernel to fp32 rounding, and the merge oracle applied to the block oracle."""
+    B, H, H_kv, Tq, Tk, D, qm, km, (rb, re) = MERGE_FUSED_CASES[case]
+    log(f"block_fwd_merge case {case}")
+    q, = draw_shape(B, H, Tq, D, torch.bfloat16, seed=40 + case, n=1)
+    k, v = draw_shape(B, H_kv, Tk, D, torch.bfloat16, seed=50 + case, n=2)
+    g = torch.Generator().manual_seed(60 + case)
+    oa0 = torch.randn(B, H, Tq, D, generator=g)
+    la0 = torch.randn(B, H, Tq, generator=g) * 2 + 3
+    la0[:, :, ::9] = -float("inf")  # running rows that have seen no key yet
+    oa0[:, :, ::9] = 0
+    o1, l1 = oa0.clone().to(DEV), la0.clone().to(DEV)
+    o2, l2 = oa0.clone().to(DEV), la0.clone().to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    cp.cpattn_block_fwd_merge(qd, kd, vd, qm, km, o1, l1, row_begin=rb, row_end=re)
+    ob = torch.empty(B, H, Tq, D, device=DEV)
+    lb = torch.empty(B, H, Tq, device=DEV)
+    if H_kv == H:
+        cp.cpattn_block_fwd(qd, kd, vd, qm, km, ob, lb, row_begin=rb, row_end=re)
+    else:
+        cp.cpattn_block_fwd_gqa(qd, kd, vd, qm, km, ob, lb, row_begin=rb, row_end=re)
+    cp.cpattn_lse_merge(o2, l2, ob, lb, rb, re)
+    torch.cuda.synchronize()
+    e_pair = max(max_err(f64(o1), f64(o2)), max_err(f64(l1), f64(l2)))
+    # oracle: block attention at global positions (KV head h // G), then the merge
+    kx = np.repeat(f64(k), H // H_kv, axis=1)
+    vx = np.repeat(f64(v), H // H_kv, axis=1)
+    O, L = oa.block_attention_fwd(f64(q)[:, :, rb:re], kx, vx, positions(qm)[rb:re], positions(km), True)
+    Om, Lm = om.lse_merge(f64(oa0)[:, :, rb:re], f64(la0)[:, :, rb:re], O, L)
+    e_o, e_l = max_err(f64(o1)[:, :, rb:re], Om), max_err(f64(l1)[:, :, rb:re], Lm)
+    log(f"  fused vs two launches {e_pair:.3g}; vs oracle O {e_o:.3g} LSE {e_l:.3g}")
+    assert e_pair <= 1e-5
+    assert e_o <= TOL_BF16 and e_l <= TOL_BF16
+    # rows outside the range are untouched
+    assert torch.equal(o1[:, :, :rb].cpu(), oa0[:, :, :rb]) and torch.equal(o1[:, :, re:].cpu(), oa0[:, :, re:])
+    assert torch.equal(l1[:, :, :rb].cpu(), la0[:, :, :rb]) and torch.equal(l1[:, :, re:].cpu(), la0[:, :, re:])
+
+
+
 FWD_CASES = [
     # B, H, Tq, Tk, D, qmap, kmap, causal, rows
     (1, 2, 300, 200, 128, (300, 150, 1000, 1300), (200, 100, 900, 1200), True, None),   # seams, ragged
@@ -449,7 +500,8 @@ def test_determinism_bitwise():
 
 def test_split_backward_and_step_driven_forward_match_bitwise():
     # cpattn_block_bwd == cpattn_block_bwd_dkdv + cpattn_block_bwd_dq, and a caller driving the ring
-    # step by step (cpattn_step_rows + cpattn_block_fwd + cpattn_lse_merge) == cpattn_ring_fwd.
+    # step by step (cpattn_step_rows + cpattn_block_fwd_merge) == cpattn_ring_fwd; the two-launch
+    # form (cpattn_block_fwd + cpattn_lse_merge) agrees to fp32 rounding.
     log("split backward / step-driven forward")
     B, H, T, D, N = 2, 3, 768, 64, 3
     q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=77, n=4)
@@ -463,8 +515,8 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
     o1 = torch.empty(B, H, Tl, D, device=DEV)
     l1 = torch.empty(B, H, Tl, device=DEV)
     cp.cpattn_ring_fwd(qr, kb, vb, maps, r, maps[r], o1, l1, ws)
-    o2 = torch.empty_like(o1)
-    l2 = torch.empty_like(l1)
+    o2, o3 = torch.empty_like(o1), torch.empty_like(o1)
+    l2, l3 = torch.empty_like(l1), torch.empty_like(l1)
     ob = torch.empty_like(o1)
     lb = torch.empty_like(l1)
     for s in range(N):
@@ -472,11 +524,17 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
         rb, _ = cp.cpattn_step_rows(maps[r], maps[src])
         if s == 0:
             cp.cpattn_block_fwd(qr, kb[src], vb[src], maps[r], maps[src], o2, l2)
+            cp.cpattn_block_fwd(qr, kb[src], vb[src], maps[r], maps[src], o3, l3)
         elif rb < Tl:
+            # the ring driver's bf16 form: one launch that merges in its epilogue
+            cp.cpattn_block_fwd_merge(qr, kb[src], vb[src], maps[r], maps[src], o2, l2, row_begin=rb)
+            # the two-launch form: block result, then the merge kernel
             cp.cpattn_block_fwd(qr, kb[src], vb[src], maps[r], maps[src], ob, lb, row_begin=rb)
-            cp.cpattn_lse_merge(o2, l2, ob, lb, rb, Tl)
+            cp.cpattn_lse_merge(o3, l3, ob, lb, rb, Tl)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # same arithmetic in another kernel: equal up to the compiler's rounding order
+    assert max_err(f64(o3), f64(o1)) <= 1e-5 and max_err(f64(l3), f64(l1)) <= 1e-5
     delta = torch.empty(B, H, Tl, device=DEV)
     cp.cpattn_bwd_preprocess(dor, o1, delta)
     acc = [torch.zeros(B, H, Tl, D, device=DEV) for _ in range(6)]
