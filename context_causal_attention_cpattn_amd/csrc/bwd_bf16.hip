@@ -106,24 +106,6 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
   const int key = kw0 + lq;                // this lane's key
   const bool key_ok = key < a.Tk;
 
-  // K and V rows of this lane's key (B operands: column = key, 8 consecutive d)
-  bf16x8 kf[C::NC], vf[C::NC];
-  {
-    const __bf16* kk = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st;
-    const __bf16* vv = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(kk + 16 * c + 8 * h) : z);
-      if constexpr (WANT_DK) vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
-    }
-  }
-  // complete the register loads before the tile loop (see the forward kernel)
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) {
-    asm volatile("" ::"v"(kf[c]));
-    if constexpr (WANT_DK) asm volatile("" ::"v"(vf[c]));
-  }
   // Positions increase with the local index, so the query rows that see this lane's key
   // are [qlo, Tq); the wave's last key has the largest qlo.
   const int qlo = a.causal ? a.qm.count_lt(a.km.pos(key_ok ? key : a.Tk - 1)) : 0;
@@ -194,6 +176,27 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (j < n_items) issue_tile(j, j);
+
+  // K and V rows of this lane's key (B operands: column = key, 8 consecutive d)
+  bf16x8 kf[C::NC], vf[C::NC];
+  {
+    const __bf16* kk = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st;
+    const __bf16* vv = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      kf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(kk + 16 * c + 8 * h) : z);
+      if constexpr (WANT_DK) vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
+    }
+  }
+  // Complete the register loads before the tile loop, so that the compiler's wait for them
+  // does not land inside it, where it would also cover later tiles in flight. They are
+  // issued after the first tiles' loads so that both take one memory round trip together.
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) {
+    asm volatile("" ::"v"(kf[c]));
+    if constexpr (WANT_DK) asm volatile("" ::"v"(vf[c]));
+  }
 
   // every query head of the group in turn: dK and dV sum over the group in registers
   for (int it = 0; it < n_items; ++it) {
@@ -405,28 +408,6 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh;
   const __bf16* vp = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh;
 
-  // ---- Q and dO rows of this lane's query (B operands), LSE and delta of the row
-  bf16x8 qf[C::NC], df[C::NC];
-  {
-    const __bf16* qq = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh + (int64_t)row * a.q.st;
-    const __bf16* dd = (const __bf16*)a.dout.p + b * a.dout.sb + hh * a.dout.sh + (int64_t)row * a.dout.st;
-#pragma unroll
-    for (int c = 0; c < C::NC; ++c) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[c] = __builtin_bit_cast(bf16x8, row_ok ? ldg16(qq + 16 * c + 8 * h) : z);
-      df[c] = __builtin_bit_cast(bf16x8, row_ok ? ldg16(dd + 16 * c + 8 * h) : z);
-    }
-  }
-  float lse2 = INFINITY, dl = 0.f;
-  if (row_ok) {
-    const float L = ((const float*)a.lse.p)[b * a.lse.sb + hh * a.lse.sh + (int64_t)row * a.lse.st];
-    lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
-    dl = ((const float*)a.delta.p)[b * a.delta.sb + hh * a.delta.sh + (int64_t)row * a.delta.st];
-  }
-  // complete the register loads before the tile loop (see the forward kernel)
-#pragma unroll
-  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]), "v"(df[c]));
-  asm volatile("" ::"v"(lse2), "v"(dl));
 
   // ---- direct global -> LDS loads: wave rb of a share fills 1 KB slots rb + NR*i of that
   // share's tiles; the rows of a lane's slots differ by a multiple of the swizzle period
@@ -473,6 +454,29 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
     if (j < n_j) issue_tile(j);
+  // ---- Q and dO rows of this lane's query (B operands), LSE and delta of the row
+  bf16x8 qf[C::NC], df[C::NC];
+  {
+    const __bf16* qq = (const __bf16*)a.q.p + b * a.q.sb + hh * a.q.sh + (int64_t)row * a.q.st;
+    const __bf16* dd = (const __bf16*)a.dout.p + b * a.dout.sb + hh * a.dout.sh + (int64_t)row * a.dout.st;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[c] = __builtin_bit_cast(bf16x8, row_ok ? ldg16(qq + 16 * c + 8 * h) : z);
+      df[c] = __builtin_bit_cast(bf16x8, row_ok ? ldg16(dd + 16 * c + 8 * h) : z);
+    }
+  }
+  float lse2 = INFINITY, dl = 0.f;
+  if (row_ok) {
+    const float L = ((const float*)a.lse.p)[b * a.lse.sb + hh * a.lse.sh + (int64_t)row * a.lse.st];
+    lse2 = L == -INFINITY ? INFINITY : L * kLog2e;
+    dl = ((const float*)a.delta.p)[b * a.delta.sb + hh * a.delta.sh + (int64_t)row * a.delta.st];
+  }
+  // complete the register loads before the tile loop; issued after the first tiles' loads,
+  // both take one memory round trip together (as in the dK/dV half)
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(qf[c]), "v"(df[c]));
+  asm volatile("" ::"v"(lse2), "v"(dl));
   wait_tiles<2 * NIQ>(min(NS - 2, n_j - 1));
   __syncthreads();
   f32x16 sA = f32x16{}, dA = f32x16{}, sB, dB;
