@@ -330,7 +330,8 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
   // rotated once instead of once per query tile.
   const bool pre = rope_table != nullptr && dtype == CPATTN_BF16;
   const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Tq, Tk, D, pre ? 1 : 0);
-  if (ring > 1 || pre) {
+  // bf16 steps merge in the block kernel's epilogue: only fp32 rings and rotary use the workspace
+  if ((ring > 1 && dtype != CPATTN_BF16) || pre) {
     if (!workspace || workspace_bytes < need)
       return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
     if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");

@@ -248,7 +248,8 @@ size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t
  * first rotates its K block into the workspace, then runs the block without
  * rotation (one more launch per step).
  * workspace: device memory of cpattn_ring_fwd_workspace_bytes(B,H,Tq,Tk,D,
- * rope) bytes, 256-byte aligned; may be NULL when ring == 1 without rotary.
+ * rope) bytes, 256-byte aligned; used by fp32 rings (ring > 1) and by the
+ * rotary form, may be NULL otherwise (bf16 without rotary, or ring == 1).
  * Other arguments as in cpattn_block_fwd.
  * Errors: as cpattn_block_fwd, plus EINVAL for ring < 1, rank out of range,
  * a short workspace.

@@ -105,11 +105,14 @@ def test_ring_fwd_rejects():
     ms = (cp.cpattn_posmap * n)(cp.cpattn_posmap(64, 32, 0, 64), cp.cpattn_posmap(64, 32, 32, 32))
     qm = cp.cpattn_posmap(64, 32, 0, 64)
     o, lse = _t(), _t(st=1)
-    args = lambda ring, rank, ws, wsb: (ctypes.byref(_t()), ks, ks, ms, ring, rank, ctypes.byref(qm), 1, 1, 1, 64, 64,
+    # fp32 inputs (dtype 0, fp32 row strides): a ring of more than one step merges through the workspace
+    t32 = _t(st=64)
+    args = lambda ring, rank, ws, wsb: (ctypes.byref(t32), ks, ks, ms, ring, rank, ctypes.byref(qm), 0, 1, 1, 64, 64,
                                         64, 1, 0.0, None, 0, ctypes.byref(o), ctypes.byref(lse), ws, wsb, None)
     assert lib.cpattn_ring_fwd(*args(0, 0, None, 0)) == -1
     assert lib.cpattn_ring_fwd(*args(2, 2, None, 0)) == -1
     assert lib.cpattn_ring_fwd(*args(2, 0, None, 0)) == -1  # no workspace
+    assert "workspace" in cp.cpattn_last_error()
     assert lib.cpattn_ring_fwd(*args(2, 0, ctypes.c_void_p(0x100010), 1 << 20)) == -1  # misaligned workspace
     assert "workspace" in cp.cpattn_last_error()
 

@@ -113,6 +113,30 @@ def test_block_fwd_merge_matches_fwd_then_merge(case):
     assert torch.equal(l1[:, :, :rb].cpu(), la0[:, :, :rb]) and torch.equal(l1[:, :, re:].cpu(), la0[:, :, re:])
 
 
+def test_block_fwd_merge_strided_accumulators():
+    """The fused merge reads and writes the running (O, LSE) through their strides: every other
+    row of a larger buffer, whose other rows stay untouched."""
+    B, H, T, D = 2, 3, 200, 128
+    log("block_fwd_merge strided accumulators")
+    q, k, v = (x.to(DEV) for x in draw_shape(B, H, T, D, torch.bfloat16, seed=71, n=3))
+    m = (T, 100, 0, 300)
+    g = torch.Generator().manual_seed(72)
+    oa0, la0 = torch.randn(B, H, T, D, generator=g), torch.randn(B, H, T, generator=g) + 4
+    big_o = torch.full((B, H, 2 * T, D), 5.0, device=DEV)
+    big_l = torch.full((B, H, 2 * T), 5.0, device=DEV)
+    o_acc, l_acc = big_o[:, :, ::2], big_l[:, :, ::2]
+    o_acc.copy_(oa0)
+    l_acc.copy_(la0)
+    cp.cpattn_block_fwd_merge(q, k, v, m, m, o_acc, l_acc)
+    ob, lb = torch.empty(B, H, T, D, device=DEV), torch.empty(B, H, T, device=DEV)
+    cp.cpattn_block_fwd(q, k, v, m, m, ob, lb)
+    o2, l2 = oa0.clone().to(DEV), la0.clone().to(DEV)
+    cp.cpattn_lse_merge(o2, l2, ob, lb, 0, T)
+    torch.cuda.synchronize()
+    assert max_err(f64(o_acc), f64(o2)) <= 1e-5 and max_err(f64(l_acc), f64(l2)) <= 1e-5
+    assert (f64(big_o)[:, :, 1::2] == 5).all() and (f64(big_l)[:, :, 1::2] == 5).all()
+
+
 
 FWD_CASES = [
     # B, H, Tq, Tk, D, qmap, kmap, causal, rows
@@ -365,6 +389,12 @@ def test_ring_fwd_all_ranks(T, N, D, dtype):
         eo, el = max_err(f64(o), O[:, :, list(pos[r])]), max_err(f64(lse), L[:, :, list(pos[r])])
         log(f"  rank {r}: max err O {eo:.3g} LSE {el:.3g}")
         assert eo <= tol(dtype) and el <= tol(dtype)
+        if dtype == torch.bfloat16:
+            # bf16 steps merge in the block kernel: no workspace needed, same result
+            o2, l2 = torch.empty_like(o), torch.empty_like(lse)
+            cp.cpattn_ring_fwd(gather(q, pos[r]), kb, vb, maps, r, maps[r], o2, l2, None)
+            torch.cuda.synchronize()
+            assert torch.equal(o2, o) and torch.equal(l2, lse)
 
 
 # ----------------------------------------------------------------------------- backward
