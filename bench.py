@@ -622,6 +622,20 @@ def main():
         torch.cuda.empty_cache()
         extra["merge_hbm_16k"] = merge_hbm_probe()
         line["other_workloads"] = extra
+        # the two throughput targets of the hot path, read off the measurements above:
+        # block forward >= 50 % of the bf16 MFMA peak (16k window, both ring steps), LSE merge
+        # >= 70 % of HBM bandwidth (its own launch in the 16k pipeline, and from HBM with the
+        # last-level cache flushed)
+        k16 = extra["win16k"]["kernels"]
+        fwd_fracs = [k16[n]["frac"] for n in ("block_fwd", "block_fwd_merge") if n in k16]
+        mrg = extra["win16k_fwd_two_launch_merge"]["kernels"].get("lse_merge", {})
+        line["targets"] = {
+            "block_fwd_bf16_peak": {"target": 0.5, "workload": "win16k", "frac_per_step": fwd_fracs,
+                                    "met": bool(fwd_fracs) and min(fwd_fracs) >= 0.5},
+            "lse_merge_hbm": {"target": 0.7, "frac_in_pipeline": mrg.get("frac"),
+                              "frac_cache_flushed": round(extra["merge_hbm_16k"]["frac_hbm"], 4),
+                              "met_in_pipeline": mrg.get("frac", 0.0) >= 0.7},
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, share)
     print(json.dumps(line))
