@@ -52,10 +52,10 @@ EXTRA_STEPS, EXTRA_WARMUP = 20, 20
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU clock ramps up over the first tens of milliseconds under load: 200 untimed steps
-    # (about 60 ms at the GPT-2-small shape) let it settle before the 100 timed ones
+    # the GPU clock ramps up under load: 1000 untimed graph replays (about 0.26 s at the
+    # GPT-2-small shape) let it settle before the 100 timed ones
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="gpt2s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
@@ -327,10 +327,15 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
     """Wall-clock time per step over ``steps`` steps (HIP-graph replays of one captured step when
     ``graph``; each replay is checked bitwise against the eager result first), then per-launch HIP
     event durations over ``steps`` eager steps queued behind a spin kernel so that the GPU never
-    waits for the host between launches."""
+    waits for the host between launches.
+
+    The ``warmup`` untimed steps run the timed path: with a graph, a few eager steps, the
+    capture, then ``warmup`` replays. Eager steps leave host gaps between launches at small
+    shapes, and after them the clock had not settled: the first timing in a process read 3 %
+    below the ones after it."""
     import torch
     share.build_plan(do_bwd)
-    for _ in range(warmup):
+    for _ in range(min(warmup, 10) if graph else warmup):
         share.step()
     torch.cuda.synchronize()
     outs = [share.o, share.lse] + ([share.dq] + share.dk + share.dv if do_bwd else [])
@@ -354,6 +359,8 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
             print(f"[bench] graph capture not used: {e}", file=sys.stderr)
             g = None
         share.build_plan(do_bwd)
+    for _ in range(warmup if g is not None else 0):
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
