@@ -335,7 +335,8 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
     below the ones after it."""
     import torch
     share.build_plan(do_bwd)
-    for _ in range(min(warmup, 10) if graph else warmup):
+    n_eager = min(warmup, 10) if graph else warmup
+    for _ in range(n_eager):
         share.step()
     torch.cuda.synchronize()
     outs = [share.o, share.lse] + ([share.dq] + share.dk + share.dv if do_bwd else [])
@@ -359,8 +360,8 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
             print(f"[bench] graph capture not used: {e}", file=sys.stderr)
             g = None
         share.build_plan(do_bwd)
-    for _ in range(warmup if g is not None else 0):
-        g.replay()
+    for _ in range(warmup if g is not None else warmup - n_eager):  # eager if capture failed
+        g.replay() if g is not None else share.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
