@@ -241,13 +241,14 @@ def test_block_fwd_rope(D):
     assert eo <= TOL_BF16 and el <= TOL_BF16
 
 
-def test_rope_rotate_in_place_strided_and_against_oracle():
+@pytest.mark.parametrize("H", [3, 8])  # one head per thread, and four heads sharing a table row
+def test_rope_rotate_in_place_strided_and_against_oracle(H):
     """One rotation at global positions (HeadTail rank 1 of 3): within one bf16 rounding of
     the fp64 rotation of the same bf16 input; in place == out of place; strided == contiguous."""
     T, N, r, D = 1200, 3, 1, 128
-    log(f"rope_rotate T={T} N={N} rank={r} D={D}")
+    log(f"rope_rotate T={T} N={N} rank={r} D={D} H={H}")
     m, pos = cp.cpattn_headtail_shard(T, N, r)
-    B, H, Tl = 2, 3, T // N
+    B, Tl = 2, T // N
     x, = draw_shape(B, H, Tl, D, torch.bfloat16, seed=77, n=1)
     tab = torch.empty(T, D, device=DEV)
     cp.cpattn_rope_table(10000.0, T, D, tab)
