@@ -48,12 +48,6 @@ def positions_from_deltas(length: int, split: int, d0: int, d1: int) -> list[int
     return [i + (d0 if i < split else d1) for i in range(length)]
 
 
-def contiguous_positions(T: int, ring: int, rank: int) -> list[int]:
-    """Plain (not load-balanced) sharding: rank r holds [r*T/N, (r+1)*T/N)."""
-    n = T // ring
-    return list(range(rank * n, (rank + 1) * n))
-
-
 def ring_source(rank: int, step: int, ring: int) -> int:
     """Owner of the KV block rank ``rank`` holds at ring step ``step``.
 

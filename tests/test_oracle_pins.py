@@ -423,6 +423,71 @@ def test_mutant_gqa_strided_grouping_is_caught():
     assert np.abs(good - bad).max() > 1e-3
 
 
+@pytest.mark.parametrize("H,H_kv", [(4, 2), (4, 1)])
+def test_gqa_causal_bwd_matches_torch_autograd(H, H_kv):
+    """gqa.causal_attention_bwd against torch float64 autograd of SDPA over K / V heads
+    gathered per query head (the gather's backward sums each KV head's group: an independent
+    library route to the group reduce of the log's 2026-07-01 entry)."""
+    T, D = 33, 8
+    q, do = (torch.from_numpy(rnd(2, H, T, D, seed=s)) for s in (170, 171))
+    k, v = (torch.from_numpy(rnd(2, H_kv, T, D, seed=s)) for s in (172, 173))
+    qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
+    idx = torch.arange(H) // (H // H_kv)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt[:, idx], vt[:, idx], is_causal=True)
+    out.backward(do)
+    dq, dk, dv, o, lse = gqa.causal_attention_bwd(q.numpy(), k.numpy(), v.numpy(), do.numpy())
+    np.testing.assert_allclose(o, out.detach().numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, qt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), atol=1e-12)
+
+
+def test_gqa_causal_bwd_finite_differences_shared_kv():
+    """gqa.causal_attention_bwd on the full sequence: central differences with respect to
+    the shared K and V heads (MQA, G = 3) and to q."""
+    H, H_kv, T, D = 3, 1, 5, 4
+    q, do = rnd(1, H, T, D, seed=174), rnd(1, H, T, D, seed=175)
+    k, v = rnd(1, H_kv, T, D, seed=176), rnd(1, H_kv, T, D, seed=177)
+    dq, dk, dv, _, _ = gqa.causal_attention_bwd(q, k, v, do)
+
+    def loss(qq, kk, vv):
+        # per query head, brute force against the KV head of its group
+        tot = []
+        for hq in range(H):
+            O, _ = brute.attention(_tolist(qq[0, hq]), _tolist(kk[0, hq * H_kv // H]),
+                                   _tolist(vv[0, hq * H_kv // H]), list(range(T)), list(range(T)))
+            tot += [o * g for orow, grow in zip(O, _tolist(do[0, hq])) for o, g in zip(orow, grow)]
+        return math.fsum(tot)
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            ap, am = dict(args), dict(args)
+            ap[name], am[name] = xp, xm
+            num[idx] = (loss(ap["q"], ap["k"], ap["v"]) - loss(am["q"], am["k"], am["v"])) / (2 * h)
+        assert np.abs(num - g).max() <= 1e-6 * max(1.0, np.abs(g).max()), name
+
+
+def test_mutant_gqa_group_mean_is_caught():
+    # planted: the group reduce takes the mean over a group's query heads instead of the
+    # sum; the torch-autograd pin above rejects it
+    H, H_kv, T, D = 4, 2, 9, 4
+    q, do = (torch.from_numpy(rnd(1, H, T, D, seed=s)) for s in (178, 179))
+    k, v = (torch.from_numpy(rnd(1, H_kv, T, D, seed=s)) for s in (180, 181))
+    kt, vt = (x.clone().requires_grad_(True) for x in (k, v))
+    idx = torch.arange(H) // (H // H_kv)
+    torch.nn.functional.scaled_dot_product_attention(q, kt[:, idx], vt[:, idx], is_causal=True).backward(do)
+    _, dk_h, dv_h, _, _ = attention.causal_attention_bwd(q.numpy(), gqa.expand_kv(k.numpy(), H),
+                                                         gqa.expand_kv(v.numpy(), H), do.numpy())
+    bad_dv = dv_h.reshape(1, H_kv, H // H_kv, T, D).mean(axis=2)
+    assert np.abs(bad_dv - vt.grad.numpy()).max() > 1e-3
+
+
 def test_bwd_matches_torch_autograd_float64():
     q, k, v, do = (torch.from_numpy(rnd(1, 2, 30, 8, seed=s)) for s in (84, 85, 86, 87))
     qt, kt, vt = (x.clone().requires_grad_(True) for x in (q, k, v))
@@ -455,9 +520,88 @@ def test_bwd_ring_accumulated_equals_unsharded(ring_n):
     np.testing.assert_allclose(rv, dv, atol=1e-12)
 
 
-def test_delta_definition():
-    do, o = rnd(3, 7, 5, seed=96), rnd(3, 7, 5, seed=97)
-    np.testing.assert_allclose(attention.delta(do, o), np.einsum("btd,btd->bt", do, o), atol=1e-14)
+def _dq_from_row_term(q, k, v, do, row_term):
+    """dQ of full-sequence causal attention (one head) with the softmax-backward row term
+    supplied by ``row_term(do, o)``; everything else from the oracle's forward."""
+    T, D = q.shape
+    sig = 1.0 / math.sqrt(D)
+    O, L = attention.causal_attention_fwd(q, k, v)
+    P = np.exp(sig * (q @ k.T) - L[:, None]) * np.tri(T)
+    dS = P * ((do @ v.T) - row_term(do, O)[:, None])
+    return sig * (dS @ k)
+
+
+def _fd_grad_q(q, k, v, do, h=1e-6):
+    """Central differences of sum(dO * O) with respect to q (O from brute force)."""
+    T, D = q.shape
+    pos = list(range(T))
+
+    def loss(qq):
+        O, _ = brute.attention(_tolist(qq), _tolist(k), _tolist(v), pos, pos)
+        return math.fsum(o * g for orow, grow in zip(O, _tolist(do)) for o, g in zip(orow, grow))
+
+    num = np.zeros_like(q)
+    for i in range(T):
+        for d in range(D):
+            qp, qm = q.copy(), q.copy()
+            qp[i, d] += h
+            qm[i, d] -= h
+            num[i, d] = (loss(qp) - loss(qm)) / (2 * h)
+    return num
+
+
+def test_delta_pinned_by_finite_differences():
+    # The row term D_p of the softmax backward (the log's 2026-03-24 "Di correction"): with
+    # attention.delta as the row term, dQ matches central differences of sum(dO * O) taken
+    # through the brute-force forward.
+    T, D = 7, 4
+    q, k, v, do = (rnd(T, D, seed=s) for s in (150, 151, 152, 153))
+    got = _dq_from_row_term(q, k, v, do, attention.delta)
+    num = _fd_grad_q(q, k, v, do)
+    assert np.abs(got - num).max() <= 1e-6 * max(1.0, np.abs(num).max())
+
+
+def test_delta_equals_probability_weighted_dp():
+    # D_p = sum_j P_pj (dO_p . v_j): the expectation of dP under the row's softmax, with
+    # P from pure-Python brute force (no numpy), for causal rows at global positions.
+    rng = np.random.default_rng(154)
+    Tq, Tk, D = 6, 9, 4
+    q, k, v, do = (rng.standard_normal((n, D)) for n in (Tq, Tk, Tk, Tq))
+    qpos, kpos = [3, 4, 5, 12, 13, 14], list(range(9))
+    O, L = brute.attention(_tolist(q), _tolist(k), _tolist(v), qpos, kpos)
+    sig = 1.0 / math.sqrt(D)
+    want = []
+    for p in range(Tq):
+        terms = []
+        for j in range(Tk):
+            if kpos[j] > qpos[p]:
+                continue
+            s = sig * math.fsum(q[p, d] * k[j, d] for d in range(D))
+            terms.append(math.exp(s - L[p]) * math.fsum(do[p, d] * v[j, d] for d in range(D)))
+        want.append(math.fsum(terms))
+    np.testing.assert_allclose(attention.delta(do, np.array(O)), want, atol=1e-13)
+
+
+def test_mutant_delta_from_block_output_is_caught():
+    # planted: the row term taken from the output of the first key block only instead of
+    # the final merged output -- the mistake the log's 2026-03-24 entry corrects
+    T, D = 7, 4
+    q, k, v, do = (rnd(T, D, seed=s) for s in (155, 156, 157, 158))
+    split = 3
+    pos = np.arange(T)
+    O_blk, _ = attention.block_attention_fwd(q, k[:split], v[:split], pos, pos[:split])
+    bad = _dq_from_row_term(q, k, v, do, lambda d, o: attention.delta(d, O_blk))
+    num = _fd_grad_q(q, k, v, do)
+    assert np.abs(bad - num).max() > 1e-3
+
+
+def test_mutant_delta_summed_over_rows_is_caught():
+    # planted: the product summed over the rows (axis -2) and broadcast back
+    T, D = 7, 7
+    q, k, v, do = (rnd(T, D, seed=s) for s in (159, 160, 161, 162))
+    bad = _dq_from_row_term(q, k, v, do, lambda d, o: (d * o).sum(axis=-2))
+    num = _fd_grad_q(q, k, v, do)
+    assert np.abs(bad - num).max() > 1e-3
 
 
 # --------------------------------------------------------------------------- planted mistakes
