@@ -148,6 +148,50 @@ def _dtype(t) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _expect(name: str, t, shape, dtype, like=None):
+    """Reject a tensor whose shape, dtype or device does not match what the kernels will
+    address: the C ABI sees pointers and strides only and cannot check buffer extents."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if like is not None and t.device != like.device:
+        raise ValueError(f"{name}: on {t.device}, expected {like.device}")
+
+
+def _inputs(q, k, v, H_kv=None):
+    """q [B,H,Tq,D] bf16 or fp32; k, v [B,H_kv,Tk,D] of q's dtype. Returns (B,H,H_kv,Tq,Tk,D)."""
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor [B, H, Tq, D]")
+    _dtype(q)
+    B, H, Tq, D = q.shape
+    if k is None or k.dim() != 4:
+        raise ValueError("k must be a 4-D tensor [B, H_kv, Tk, D]")
+    Hk, Tk = k.shape[1], k.shape[2]
+    if H_kv is not None and Hk != H_kv:
+        raise ValueError(f"k has {Hk} heads, expected {H_kv}")
+    _expect("k", k, (B, Hk, Tk, D), q.dtype, q)
+    _expect("v", v, (B, Hk, Tk, D), q.dtype, q)
+    return B, H, Hk, Tq, Tk, D
+
+
+def _rope_check(rope_table, D, like):
+    if rope_table is None:
+        return
+    if rope_table.dim() != 2 or rope_table.shape[1] != D:
+        raise ValueError(f"rope_table: shape {tuple(rope_table.shape)}, expected [rows, {D}]")
+    _expect("rope_table", rope_table, rope_table.shape, _f32(), like)
+    if not rope_table.is_contiguous():
+        raise ValueError("rope_table must be contiguous")
+
+
 def cpattn_version() -> int:
     return load().cpattn_version()
 
@@ -181,8 +225,10 @@ def _rope_args(rope_table):
 def cpattn_block_fwd(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: float = 0.0, rope_table=None,
                      row_begin: int = 0, row_end: int | None = None, stream=None):
     """O, LSE of rows [row_begin, row_end) of q against one KV block (rope_table: [rows, D] fp32)."""
-    B, H, Tq, D = q.shape
-    Tk = k.shape[2]
+    B, H, _, Tq, Tk, D = _inputs(q, k, v, q.shape[1] if q is not None and q.dim() == 4 else None)
+    _expect("o", o, (B, H, Tq, D), _f32(), q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _rope_check(rope_table, D, q)
     rp, rr = _rope_args(rope_table)
     _check(load().cpattn_block_fwd(
         _tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, Tq, Tk, D, _map(qmap), _map(kmap), int(causal),
@@ -191,7 +237,13 @@ def cpattn_block_fwd(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: fl
 
 
 def cpattn_lse_merge(o_acc, lse_acc, o_blk, lse_blk, row_begin: int = 0, row_end: int | None = None, stream=None):
+    if o_acc is None or o_acc.dim() != 4:
+        raise ValueError("o_acc must be a 4-D tensor [B, H, T, D]")
     B, H, T, D = o_acc.shape
+    _expect("o_acc", o_acc, (B, H, T, D), _f32())
+    _expect("lse_acc", lse_acc, (B, H, T), _f32(), o_acc)
+    _expect("o_blk", o_blk, (B, H, T, D), _f32(), o_acc)
+    _expect("lse_blk", lse_blk, (B, H, T), _f32(), o_acc)
     _check(load().cpattn_lse_merge(_tensor(o_acc), _tensor(lse_acc, 3), _tensor(o_blk), _tensor(lse_blk, 3), B, H, T,
                                    D, row_begin, T if row_end is None else row_end, _stream(stream)))
 
@@ -209,8 +261,15 @@ def cpattn_ring_fwd_workspace_bytes(B: int, H: int, Tq: int, D: int, Tk: int | N
 
 def cpattn_rope_rotate(x, qmap, rope_table, out=None, stream=None):
     """out (default: x itself) = x rotated row by row at the global positions of ``qmap``."""
+    if x is None or x.dim() != 4:
+        raise ValueError("x must be a 4-D tensor [B, H, T, D]")
+    _dtype(x)
     B, H, T, D = x.shape
     out = x if out is None else out
+    _expect("out", out, (B, H, T, D), x.dtype, x)
+    if rope_table is None:
+        raise ValueError("rope_table is required")
+    _rope_check(rope_table, D, x)
     rp, rr = _rope_args(rope_table)
     _check(load().cpattn_rope_rotate(_tensor(x), _dtype(x), B, H, T, D, _map(qmap), rp, rr, _tensor(out),
                                      _stream(stream)))
@@ -219,7 +278,13 @@ def cpattn_rope_rotate(x, qmap, rope_table, out=None, stream=None):
 
 def cpattn_rope_rotate_grad(g, qmap, rope_table, stream=None):
     """In place: g (fp32, gradient with respect to rotated rows) <- R(pos)^T g."""
+    if g is None or g.dim() != 4:
+        raise ValueError("g must be a 4-D tensor [B, H, T, D]")
     B, H, T, D = g.shape
+    _expect("g", g, (B, H, T, D), _f32())
+    if rope_table is None:
+        raise ValueError("rope_table is required")
+    _rope_check(rope_table, D, g)
     rp, rr = _rope_args(rope_table)
     _check(load().cpattn_rope_rotate_grad(_tensor(g), B, H, T, D, _map(qmap), rp, rr, _stream(stream)))
     return g
@@ -231,8 +296,17 @@ def cpattn_ring_fwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, 
     n = len(k_blocks)
     if len(v_blocks) != n or len(kmaps) != n:
         raise ValueError("k_blocks, v_blocks, kmaps must have the same length")
-    B, H, Tq, D = q.shape
-    Tk = k_blocks[0].shape[2]
+    if n < 1:
+        raise ValueError("at least one KV block is needed")
+    B, H, _, Tq, Tk, D = _inputs(q, k_blocks[0], v_blocks[0], q.shape[1] if q is not None and q.dim() == 4 else None)
+    for i in range(n):
+        _expect(f"k_blocks[{i}]", k_blocks[i], (B, H, Tk, D), q.dtype, q)
+        _expect(f"v_blocks[{i}]", v_blocks[i], (B, H, Tk, D), q.dtype, q)
+    _expect("o_acc", o_acc, (B, H, Tq, D), _f32(), q)
+    _expect("lse_acc", lse_acc, (B, H, Tq), _f32(), q)
+    _rope_check(rope_table, D, q)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace: on {workspace.device}, expected {q.device}")
     ks = (cpattn_tensor * n)(*[_tensor(t) for t in k_blocks])
     vs = (cpattn_tensor * n)(*[_tensor(t) for t in v_blocks])
     ms = (cpattn_posmap * n)(*[_map(m) for m in kmaps])
@@ -256,8 +330,20 @@ def cpattn_ring_bwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, 
     n = len(k_blocks)
     if len(v_blocks) != n or len(kmaps) != n or len(dk_blocks) != n or len(dv_blocks) != n:
         raise ValueError("k_blocks, v_blocks, kmaps, dk_blocks, dv_blocks must have the same length")
-    B, H, Tq, D = q.shape
-    Tk = k_blocks[0].shape[2]
+    if n < 1:
+        raise ValueError("at least one KV block is needed")
+    B, H, _, Tq, Tk, D = _inputs(q, k_blocks[0], v_blocks[0], q.shape[1] if q is not None and q.dim() == 4 else None)
+    for i in range(n):
+        _expect(f"k_blocks[{i}]", k_blocks[i], (B, H, Tk, D), q.dtype, q)
+        _expect(f"v_blocks[{i}]", v_blocks[i], (B, H, Tk, D), q.dtype, q)
+        _expect(f"dk_blocks[{i}]", dk_blocks[i], (B, H, Tk, D), _f32(), q)
+        _expect(f"dv_blocks[{i}]", dv_blocks[i], (B, H, Tk, D), _f32(), q)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("o", o, (B, H, Tq, D), _f32(), q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace: on {workspace.device}, expected {q.device}")
     ks = (cpattn_tensor * n)(*[_tensor(t) for t in k_blocks])
     vs = (cpattn_tensor * n)(*[_tensor(t) for t in v_blocks])
     dks = (cpattn_tensor * n)(*[_tensor(t) for t in dk_blocks])
@@ -271,15 +357,25 @@ def cpattn_ring_bwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, 
 
 
 def cpattn_bwd_preprocess(dout, o, delta, stream=None):
+    if dout is None or dout.dim() != 4:
+        raise ValueError("dout must be a 4-D tensor [B, H, Tq, D]")
+    _dtype(dout)
     B, H, Tq, D = dout.shape
+    _expect("o", o, (B, H, Tq, D), _f32(), dout)
+    _expect("delta", delta, (B, H, Tq), _f32(), dout)
     _check(load().cpattn_bwd_preprocess(_tensor(dout), _dtype(dout), _tensor(o), _tensor(delta, 3), B, H, Tq, D,
                                         _stream(stream)))
 
 
 def cpattn_block_bwd(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
                      scale: float = 0.0, accumulate: bool = True, stream=None):
-    B, H, Tq, D = q.shape
-    Tk = k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v, q.shape[1] if q is not None and q.dim() == 4 else None)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("delta", delta, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
+    _expect("dk_acc", dk_acc, (B, H_kv, Tk, D), _f32(), q)
+    _expect("dv_acc", dv_acc, (B, H_kv, Tk, D), _f32(), q)
     _check(load().cpattn_block_bwd(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                    _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq, Tk,
                                    D, _map(qmap), _map(kmap), int(causal), float(scale), int(accumulate),
@@ -288,8 +384,12 @@ def cpattn_block_bwd(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, km
 
 def cpattn_block_bwd_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
                           scale: float = 0.0, accumulate: bool = True, stream=None):
-    B, H, Tq, D = q.shape
-    Tk = k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v, q.shape[1] if q is not None and q.dim() == 4 else None)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("delta", delta, (B, H, Tq), _f32(), q)
+    _expect("dk_acc", dk_acc, (B, H_kv, Tk, D), _f32(), q)
+    _expect("dv_acc", dv_acc, (B, H_kv, Tk, D), _f32(), q)
     _check(load().cpattn_block_bwd_dkdv(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q),
                                         _tensor(lse, 3), _tensor(delta, 3), _tensor(dk_acc), _tensor(dv_acc), B, H, Tq,
                                         Tk, D, _map(qmap), _map(kmap), int(causal), float(scale), int(accumulate),
@@ -298,8 +398,11 @@ def cpattn_block_bwd_dkdv(q, k, v, dout, lse, delta, dk_acc, dv_acc, qmap, kmap,
 
 def cpattn_block_bwd_dq(q, k, v, dout, lse, delta, dq_acc, qmap, kmap, causal: bool = True, scale: float = 0.0,
                         accumulate: bool = True, stream=None):
-    B, H, Tq, D = q.shape
-    Tk = k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v, q.shape[1] if q is not None and q.dim() == 4 else None)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("delta", delta, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
     _check(load().cpattn_block_bwd_dq(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                       _tensor(delta, 3), _tensor(dq_acc), B, H, Tq, Tk, D, _map(qmap), _map(kmap),
                                       int(causal), float(scale), int(accumulate), _stream(stream)))
@@ -308,8 +411,10 @@ def cpattn_block_bwd_dq(q, k, v, dout, lse, delta, dq_acc, qmap, kmap, causal: b
 def cpattn_block_fwd_gqa(q, k, v, qmap, kmap, o, lse, causal: bool = True, scale: float = 0.0, rope_table=None,
                          row_begin: int = 0, row_end: int | None = None, stream=None):
     """Grouped-query block forward: q [B,H,Tq,D], k / v [B,H_kv,Tk,D], query head h uses KV head h // (H // H_kv)."""
-    B, H, Tq, D = q.shape
-    H_kv, Tk = k.shape[1], k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v)
+    _expect("o", o, (B, H, Tq, D), _f32(), q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _rope_check(rope_table, D, q)
     rp, rr = _rope_args(rope_table)
     row_end = Tq if row_end is None else row_end
     _check(load().cpattn_block_fwd_gqa(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
@@ -321,8 +426,9 @@ def cpattn_block_fwd_merge(q, k, v, qmap, kmap, o_acc, lse_acc, causal: bool = T
                            row_begin: int = 0, row_end: int | None = None, stream=None):
     """Block forward of rows [row_begin, row_end) folded into the running (o_acc, lse_acc) in one launch
     (k / v may have fewer heads than q: grouped-query)."""
-    B, H, Tq, D = q.shape
-    H_kv, Tk = k.shape[1], k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v)
+    _expect("o_acc", o_acc, (B, H, Tq, D), _f32(), q)
+    _expect("lse_acc", lse_acc, (B, H, Tq), _f32(), q)
     row_end = Tq if row_end is None else row_end
     _check(load().cpattn_block_fwd_merge(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
                                          _map(qmap), _map(kmap), int(causal), float(scale), row_begin, row_end,
@@ -332,8 +438,13 @@ def cpattn_block_fwd_merge(q, k, v, qmap, kmap, o_acc, lse_acc, causal: bool = T
 def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,
                          scale: float = 0.0, accumulate: bool = True, stream=None):
     """Grouped-query block backward: dk_acc / dv_acc per KV head, summed over each group."""
-    B, H, Tq, D = q.shape
-    H_kv, Tk = k.shape[1], k.shape[2]
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v, None)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("delta", delta, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
+    _expect("dk_acc", dk_acc, (B, H_kv, Tk, D), _f32(), q)
+    _expect("dv_acc", dv_acc, (B, H_kv, Tk, D), _f32(), q)
     _check(load().cpattn_block_bwd_gqa(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q), _tensor(lse, 3),
                                        _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H,
                                        H_kv, Tq, Tk, D, _map(qmap), _map(kmap), int(causal), float(scale),

@@ -42,6 +42,11 @@
  *     returns a message (thread-local). Arguments are validated before any
  *     launch; on error nothing is launched. Faults inside a kernel surface at
  *     the caller's next synchronisation.
+ *   - The library sees pointers and strides, not allocations: the caller
+ *     guarantees that every tensor holds the elements its sizes and strides
+ *     address, in the dtype the call states (inputs in `dtype`, outputs and
+ *     accumulators fp32). The Python binding checks each tensor's shape,
+ *     dtype and device against these before it calls in.
  *   - Stateless and thread-safe; concurrent calls on different streams must
  *     not write the same memory.
  */
