@@ -1,13 +1,34 @@
 """Helpers shared by the GPU parity tests (plumbing only: no attention math)."""
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
 
 TOL_F32 = 1e-4   # max-abs error for fp32 inputs
 TOL_BF16 = 2e-2  # max-abs error for bf16 inputs with fp32 accumulation
+
+
+def tol_bf16_scaled(ref) -> float:
+    """Bound for bf16-input outputs whose reference exceeds 1 in magnitude: 2e-2 times that
+    magnitude (equal absolute and relative tolerance, the convention of the RL-Kernel linear
+    logp runbook's bf16 gate against an fp32-accumulation reference, "Reading Output").
+    The kernels round P and dS to bf16 before their fp32-accumulating products, so their
+    error grows with the output's own scale; for outputs within [-1, 1] this is TOL_BF16."""
+    return TOL_BF16 * max(1.0, float(np.abs(np.asarray(ref)).max()))
+
+
+def per_head(fn, heads, workers: int | None = None):
+    """[fn(h) for h in heads], run in a thread pool with one BLAS thread per call: numpy
+    releases the interpreter lock in its array loops, so independent heads of the fp64
+    oracle run in parallel on the host's cores."""
+    from threadpoolctl import threadpool_limits
+    n = workers or min(16, len(os.sched_getaffinity(0)), len(heads))
+    with threadpool_limits(1), ThreadPoolExecutor(max(1, n)) as ex:
+        return list(ex.map(fn, heads))
 
 
 def log(msg: str):

@@ -2,8 +2,10 @@
 benchmark times (the ring driver, then the backward preprocess and one block
 backward per ring step), against the fp64 oracle.
 
-The kernels always run on every head; for the large workloads the oracle
-recomputes a sample of heads in full (every row and column of those heads).
+The kernels always run on every head. The forward of every workload is
+compared on every head; the 16k backward on four heads spread over the grid
+(first, last and two between), both ranks, every row and key of those heads.
+The oracle runs one head per host thread.
 """
 import numpy as np
 import pytest
@@ -14,7 +16,7 @@ from oracle import attention as oa
 from oracle import rope as orope
 from workloads import BY_NAME, draw
 
-from _util import TOL_BF16, TOL_F32, f64, gather, log, max_err
+from _util import TOL_BF16, TOL_F32, f64, gather, log, max_err, per_head
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -56,16 +58,25 @@ class Share:
                                 dv[src], self.maps[r], self.maps[src])
 
 
-def check_fwd(share, t64, heads, tol, rope_theta=0.0):
+def oracle_fwd(t, rows, heads, rope_theta=0.0):
+    """fp64 O [B, len(heads), rows, D] and LSE of the global causal attention for the given
+    query rows, one head per host thread (rotary applied at every global position first)."""
+    def one(h):
+        q, k, v = (f64(t[n][:, h:h + 1]) for n in ("q", "k", "v"))
+        if rope_theta:
+            allpos = np.arange(q.shape[2])
+            q, k = orope.rope_apply(q, allpos, rope_theta), orope.rope_apply(k, allpos, rope_theta)
+        return oa.causal_attention_fwd(q, k, v, rows=rows)
+    res = per_head(one, list(heads))
+    return np.concatenate([r[0] for r in res], axis=1), np.concatenate([r[1] for r in res], axis=1)
+
+
+def check_fwd(share, t, heads, tol, rope_theta=0.0, ref=None):
     rows = list(share.pos[share.rank])
-    q, k, v = t64["q"], t64["k"], t64["v"]
-    if rope_theta:
-        allpos = np.arange(q.shape[2])
-        q, k = orope.rope_apply(q, allpos, rope_theta), orope.rope_apply(k, allpos, rope_theta)
-    O, L = oa.causal_attention_fwd(q, k, v, rows=rows)
+    O, L = ref if ref is not None else oracle_fwd(t, rows, heads, rope_theta)
     eo = max_err(f64(share.o[:, heads]), O)
     el = max_err(f64(share.lse[:, heads]), L)
-    log(f"  rank {share.rank}: max err O {eo:.3g} LSE {el:.3g} (heads {heads})")
+    log(f"  rank {share.rank}: max err O {eo:.3g} LSE {el:.3g} ({len(heads)} heads)")
     assert eo <= tol and el <= tol
     return O, L
 
@@ -74,12 +85,11 @@ def test_tiny_fp32_both_ranks():
     w = BY_NAME["tiny"]
     log(f"workload {w.name}")
     t = draw(w)
-    t64 = {n: f64(x) for n, x in t.items()}
     for r in range(w.ring):
         s = Share(w, t, r)
         s.forward()
         torch.cuda.synchronize()
-        check_fwd(s, t64, slice(None), TOL_F32)
+        check_fwd(s, t, list(range(w.H)), TOL_F32)
 
 
 def test_gpt2s_rank0_forward_and_backward():
@@ -95,7 +105,7 @@ def test_gpt2s_rank0_forward_and_backward():
     s.forward()
     s.backward(dk, dv)
     torch.cuda.synchronize()
-    O, L = check_fwd(s, t64, slice(None), TOL_BF16)
+    O, L = check_fwd(s, t, list(range(w.H)), TOL_BF16)
     rows = list(s.pos[0])
     gq, gk, gv = oa.block_attention_bwd(t64["q"][:, :, rows], t64["k"], t64["v"], t64["do"][:, :, rows], O, L, rows,
                                         np.arange(w.T))
@@ -114,21 +124,53 @@ def test_win16k_rank0_forward():
     s = Share(w, t, 0)
     s.forward()
     torch.cuda.synchronize()
-    heads = [0, 31]
-    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
-    check_fwd(s, t64, heads, TOL_BF16)
+    check_fwd(s, t, list(range(w.H)), TOL_BF16)
+
+
+_WIN32K = {}
+
+
+def _win32k_reference():
+    """Inputs and the rank-0 fp64 reference (every head) of the 32k window with rotary."""
+    if not _WIN32K:
+        w = BY_NAME["win32k"]
+        t = draw(w)
+        _, pos = cp.cpattn_headtail_shard(w.T, w.ring, 0)
+        _WIN32K.update(t=t, ref=oracle_fwd(t, list(pos), range(w.H), w.rope_theta))
+    return _WIN32K["t"], _WIN32K["ref"]
 
 
 def test_win32k_rope_rank0_forward():
+    """The ring driver's rotary form: Q and each K block rotated once, then the block kernels
+    (the form the benchmark times)."""
     w = BY_NAME["win32k"]
     log(f"workload {w.name}")
-    t = draw(w)
+    t, ref = _win32k_reference()
     s = Share(w, t, 0, rope=True)
     s.forward()
     torch.cuda.synchronize()
-    heads = [9]
-    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
-    check_fwd(s, t64, heads, TOL_BF16, rope_theta=w.rope_theta)
+    check_fwd(s, t, list(range(w.H)), TOL_BF16, ref=ref)
+
+
+def test_win32k_fused_rotary_block_fwd_rank0():
+    """cpattn_block_fwd with the rotary table (the per-tile fused rotation) at the 32k window's
+    full size: step 0 on the own block, step 1 on the other block's visible rows into a second
+    pair, then cpattn_lse_merge; every head against the same reference."""
+    w = BY_NAME["win32k"]
+    log(f"workload {w.name}, fused rotary block forward")
+    t, ref = _win32k_reference()
+    s = Share(w, t, 0, rope=True)
+    Tl = w.local_len
+    cp.cpattn_block_fwd(s.q, s.kb[0], s.vb[0], s.maps[0], s.maps[0], s.o, s.lse, rope_table=s.tab)
+    src = (0 - 1) % w.ring
+    rb, _ = cp.cpattn_step_rows(s.maps[0], s.maps[src])
+    ob = torch.empty_like(s.o)
+    lb = torch.empty_like(s.lse)
+    cp.cpattn_block_fwd(s.q, s.kb[src], s.vb[src], s.maps[0], s.maps[src], ob, lb, rope_table=s.tab,
+                        row_begin=rb, row_end=Tl)
+    cp.cpattn_lse_merge(s.o, s.lse, ob, lb, rb, Tl)
+    torch.cuda.synchronize()
+    check_fwd(s, t, list(range(w.H)), TOL_BF16, ref=ref)
 
 
 def test_bwd16k_all_ranks():
@@ -144,9 +186,10 @@ def test_bwd16k_all_ranks():
         s.backward(dk, dv)
         shares.append(s)
     torch.cuda.synchronize()
-    heads = [3]
-    t64 = {n: f64(x[:, heads]) for n, x in t.items()}
-    dQ, dK, dV, O, L = oa.causal_attention_bwd(t64["q"], t64["k"], t64["v"], t64["do"])
+    heads = [0, 11, 20, 31]
+    res = per_head(lambda h: oa.causal_attention_bwd(*(f64(t[n][:, h:h + 1]) for n in ("q", "k", "v", "do"))),
+                   heads)
+    dQ, dK, dV, O, L = (np.concatenate([r[i] for r in res], axis=1) for i in range(5))
     for s in shares:
         rows = list(s.pos[s.rank])
         eo = max_err(f64(s.o[:, heads]), O[:, :, rows])
@@ -154,7 +197,7 @@ def test_bwd16k_all_ranks():
         eq = max_err(f64(s.dq[:, heads]), dQ[:, :, rows])
         ek = max_err(f64(dk[s.rank][:, heads]), dK[:, :, rows])
         ev = max_err(f64(dv[s.rank][:, heads]), dV[:, :, rows])
-        log(f"  rank {s.rank}: O {eo:.3g} LSE {el:.3g} dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
+        log(f"  rank {s.rank}, heads {heads}: O {eo:.3g} LSE {el:.3g} dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
         assert max(eo, el, eq, ek, ev) <= TOL_BF16
 
 

@@ -16,7 +16,7 @@ from oracle import rope as orope
 from oracle import shard as osh
 from workloads import draw_shape
 
-from _util import TOL_BF16, TOL_F32, f64, gather, log, max_err
+from _util import tol_bf16_scaled, TOL_BF16, TOL_F32, f64, gather, log, max_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -498,12 +498,12 @@ def test_block_bwd_tiny_and_degenerate_sizes(Tq, Tk, causal, D):
     # The kernels round P and dS to bf16 (relative 2^-9) before the fp32-accumulating
     # products, so the error scales with the output: with three keys a key's dK/dV sums 130
     # rows at weights near 1/3 and reaches |dV| ~ 20, where the measured error is 0.17 %
-    # (rms, relative) of the reference. The bound is the bf16 tolerance, or 1 % of the
-    # largest reference value where that is larger.
+    # (rms, relative) of the reference. Outputs beyond unit scale take the bf16 tolerance
+    # relative to their magnitude (tol_bf16_scaled); within it, the plain 2e-2.
     for got in (whole, halves):
         for t, r, name in zip(got, (gq, gk, gv), ("dq", "dk", "dv")):
             e = max_err(f64(t), r)
-            assert e <= max(TOL_BF16, 1e-2 * float(np.abs(r).max())), (name, e)
+            assert e <= tol_bf16_scaled(r), (name, e)
     for a_, b_ in zip(whole, halves):
         assert torch.equal(a_, b_)
 
