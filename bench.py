@@ -1,34 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of one rank's share of causal ring attention under HeadTail sharding.
 
-A step is one pass of the whole hot path over one batch of synthetic input,
-for rank 0 of the GPT-2-small-shaped workload (B=4, H=12, D=64, T=4096, ring
-degree 4; bf16 inputs, fp32 accumulation), with every KV block resident in HBM:
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is rank 0 of the 32k window with rotary (B=1, H=16,
+D=128, T=32768, ring degree 2; bf16 inputs, fp32 accumulation), every KV block
+resident in HBM:
 
-  * for each ring step s (block owner src = -s mod 4): classify the step
-    (cpattn_step_rows), block forward of the visible rows (step 0 straight into
-    the accumulator), LSE merge of those rows (steps >= 1);
-  * backward preprocess delta = rowsum(dO * O);
-  * for each ring step: the block backward (cpattn_block_bwd: dK/dV and dQ
-    halves in one grid at D = 64), accumulating in fp32 (accumulators cleared
-    once at the start of the step).
+  * Q rotated once at its global positions (cpattn_rope_rotate);
+  * for each ring step s (block owner src = -s mod 2): the block's keys rotated
+    at the owner's positions, then the block forward of the visible rows --
+    step 0 straight into the running (O, LSE), step 1 with the LSE merge in the
+    block kernel's epilogue (cpattn_block_fwd_merge).
+
+``--workload gpt2s`` (and the other workloads) time their own steps; those with
+a backward add the preprocess and one block backward per ring step.
 
 Throughput is causal-effective: only visible (query, key) pairs count, at
-4*D flops per pair for the forward and 10*D for the backward. Every launch of
-the timed steps is bracketed by HIP events on the stream the library runs on,
-which gives each kernel's average duration for the roofline object. The fp64
-CPU oracle is timed on a bounded sample of the same workload for the
-cpu_baseline object.
+4*D flops per pair for the forward and 10*D for the backward; the rotation is
+not credited. Every launch of the evented steps is bracketed by HIP events on
+the stream the library runs on, which gives each kernel's average duration for
+the roofline object. The fp64 CPU oracle is timed on a bounded sample of the
+same workload for the cpu_baseline object.
 
 Prints ONE JSON line. Only one GPU is supported.
 
-Two helper modes serve the roofline's measured HBM traffic:
+Helper modes serve the measured HBM traffic:
   --pmc-run      a few eager steps, then a plain 512 MiB device-to-device copy,
                  to run under rocprofv3 --pmc FETCH_SIZE (and again WRITE_SIZE);
+  --pmc-merge    the merge at the 16k-window shape with the last-level cache
+                 flushed before each launch, then the same calibration copy;
   --traffic-from FETCH_CSV WRITE_CSV
-                 turns the two counter-collection CSVs into profiles/traffic.json:
-                 the dominant kernel's KiB per dispatch, each counter scaled by
-                 the bytes the copy moves over what that counter read for it.
+                 turns the two counter-collection CSVs into a traffic file
+                 (profiles/traffic.json, or --traffic PATH): the kernel's KiB per
+                 dispatch, each counter scaled by the bytes the copy moves over
+                 what that counter read for it.
 """
 from __future__ import annotations
 
@@ -43,10 +48,11 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
-# the larger workloads: 20 untimed steps (100-200 ms of load) let the clock settle after their
-# inputs were generated on the host; with 1 warm-up and 3 timed steps the per-kernel figures
-# read up to 8 % low
+# the other workloads of the line: 20 untimed steps (100-200 ms of load) let the clock settle
+# after their inputs were generated on the host; with 1 warm-up and 3 timed steps the
+# per-kernel figures read up to 8 % low
 EXTRA_STEPS, EXTRA_WARMUP = 20, 20
+HEADLINE = "win32k"
 
 
 def parse():
@@ -55,13 +61,21 @@ def parse():
     # the GPU clock ramps up under load: 1000 untimed graph replays (about 0.26 s at the
     # GPT-2-small shape) let it settle before the 100 timed ones
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="gpt2s")
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--bwd", choices=("auto", "yes", "no"), default="auto",
+                    help="include the backward in a step (auto: only for workloads that draw dO or have no "
+                         "rotary, i.e. every workload but the 32k window)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads and the merge HBM probe")
     ap.add_argument("--no-graph", action="store_true", help="time eager steps instead of graph replays")
     ap.add_argument("--pmc-run", action="store_true",
                     help="counter-collection run: eager steps, then the calibration copy")
+    ap.add_argument("--pmc-merge", action="store_true",
+                    help="counter-collection run of the merge with the cache flushed, then the calibration copy")
+    ap.add_argument("--traffic-kernel", default=None,
+                    help="timed launch name whose kernels --traffic-from reads (default: the workload's "
+                         "dominant one)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic file from two rocprofv3 counter-collection CSVs")
     ap.add_argument("--separate-merge", action="store_true",
@@ -302,6 +316,29 @@ class EventLog:
 
         return _C()
 
+    # launch names that run the same GPU kernel (one template instance per head size):
+    # the roofline object reports the kernel over all its launches
+    FAMILY = {"block_fwd": "block_fwd", "block_fwd_merge": "block_fwd"}
+
+    def families(self, summary):
+        """Per-kernel totals over the launch names that share it (same shape as summary())."""
+        fam = {}
+        for name, d in summary.items():
+            f = self.FAMILY.get(name, name)
+            e = fam.setdefault(f, {"bound": d["bound"], "launches": 0, "total_ms": 0.0, "work": 0.0,
+                                   "unit": d["unit"], "peak": d["peak"], "names": []})
+            e["launches"] += d["launches"]
+            e["total_ms"] += d["total_ms"]
+            e["work"] += d["work_per_launch"] * d["launches"]
+            e["names"].append(name)
+        for e in fam.values():
+            sec = e["total_ms"] / 1e3
+            e["achieved"] = e["work"] / sec / (1e12 if e["unit"] == "TFLOP/s" else 1e9)
+            e["frac"] = e["achieved"] / e["peak"]
+            e["avg_us"] = 1e3 * e["total_ms"] / e["launches"]
+            e["work_per_launch"] = e["work"] / e["launches"]
+        return fam
+
     def summary(self):
         out = {}
         for name, work, a, b in self.rec:
@@ -382,34 +419,50 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
     return wall, ev.summary(), g is not None
 
 
-def merge_hbm_probe(reps=20):
+class MergeProbe:
     """The merge at the 16k-window shape (131072 rows, D=128: 202.9 MB) with the 256 MB
-    last-level cache flushed before each timed launch, next to a device copy (torch
-    ``copy_``) that moves the same number of bytes under the same protocol. The flush
-    writes 512 MB and then reads another 512 MB, so the written lines are evicted (and
-    written back) before the timed launch instead of during it."""
-    import torch
+    last-level cache flushed before each launch. The flush writes 512 MB and then reads
+    another 512 MB, so the written lines are evicted (and written back) before the timed
+    launch instead of during it. Beside it, under the same protocol and on the same byte
+    count: a device copy (half the bytes read, half written) and an elementwise add
+    c = a + b (two thirds read, one third written: the merge's own 2:1 mix, which reads
+    O_acc, O_blk and both LSE rows and writes O_acc and LSE_acc)."""
 
-    import context_causal_attention_cpattn_amd as cp
-    dev = torch.device("cuda:0")
-    B, H, T, D = 1, 32, 8192, 128
-    rb = 4096
-    g = torch.Generator(device=dev).manual_seed(5)
-    o_acc = torch.randn(B, H, T, D, device=dev, generator=g)
-    o_blk = torch.randn(B, H, T, D, device=dev, generator=g)
-    l_acc = torch.randn(B, H, T, device=dev, generator=g)
-    l_blk = torch.randn(B, H, T, device=dev, generator=g)
-    flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
-    flush_read = torch.ones(512 * 1024 * 1024 // 4, device=dev)
-    nbytes = B * H * (T - rb) * (12 * D + 12)
-    src = torch.ones(nbytes // 8, device=dev)  # read half the bytes, write the other half
-    dst = torch.empty_like(src)
+    def __init__(self):
+        import torch
 
-    def median_us(fn):
+        import context_causal_attention_cpattn_amd as cp
+        self.cp = cp
+        dev = torch.device("cuda:0")
+        B, H, T, D = 1, 32, 8192, 128
+        self.rb, self.T = 4096, T
+        g = torch.Generator(device=dev).manual_seed(5)
+        self.o_acc = torch.randn(B, H, T, D, device=dev, generator=g)
+        self.o_blk = torch.randn(B, H, T, D, device=dev, generator=g)
+        self.l_acc = torch.randn(B, H, T, device=dev, generator=g)
+        self.l_blk = torch.randn(B, H, T, device=dev, generator=g)
+        self.flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+        self.flush_read = torch.ones(512 * 1024 * 1024 // 4, device=dev)
+        self.rows = B * H * (T - self.rb)
+        self.nbytes = self.rows * (12 * D + 12)
+        self.src = torch.ones(self.nbytes // 8, device=dev)  # copy: read half the bytes, write the other half
+        self.dst = torch.empty_like(self.src)
+        n3 = self.nbytes // 12
+        self.a, self.b = torch.ones(n3, device=dev), torch.ones(n3, device=dev)  # add: 2/3 read, 1/3 written
+        self.c = torch.empty(n3, device=dev)
+
+    def flush_cache(self, i):
+        self.flush.fill_(float(i))
+        self.flush_read.sum()
+
+    def merge(self):
+        self.cp.cpattn_lse_merge(self.o_acc, self.l_acc, self.o_blk, self.l_blk, self.rb, self.T)
+
+    def median_us(self, fn, reps=20):
+        import torch
         times = []
         for i in range(reps + 3):
-            flush.fill_(float(i))
-            flush_read.sum()
+            self.flush_cache(i)
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
@@ -421,31 +474,84 @@ def merge_hbm_probe(reps=20):
         times.sort()
         return times[len(times) // 2] * 1e3
 
-    med = median_us(lambda: cp.cpattn_lse_merge(o_acc, l_acc, o_blk, l_blk, rb, T))
-    cop = median_us(lambda: dst.copy_(src))
-    gbs, copy_gbs = nbytes / med / 1e3, nbytes / cop / 1e3
-    return {"rows": B * H * (T - rb), "bytes": nbytes, "median_us": med, "GB/s": gbs,
-            "frac_hbm": gbs / PEAK_HBM_GBS, "copy_GB/s": copy_gbs, "frac_of_copy": gbs / copy_gbs,
-            "note": "before each launch 512 MB written, then another 512 MB read, to evict the 256 MB "
-                    "last-level cache; the copy moves the same bytes (half read, half written) under the "
-                    "same protocol"}
+    def run(self):
+        import torch
+        med = self.median_us(self.merge)
+        cop = self.median_us(lambda: self.dst.copy_(self.src))
+        add = self.median_us(lambda: torch.add(self.a, self.b, out=self.c))
+        nb = self.nbytes
+        gbs, copy_gbs, add_gbs = nb / med / 1e3, nb / cop / 1e3, nb / add / 1e3
+        return {"rows": self.rows, "bytes": nb, "median_us": med, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+                "copy_GB/s": copy_gbs, "frac_of_copy": gbs / copy_gbs,
+                "stream_2to1_GB/s": add_gbs, "frac_of_stream_2to1": gbs / add_gbs,
+                "note": "before each launch 512 MB written, then another 512 MB read, to evict the 256 MB "
+                        "last-level cache; the copy (half read, half written) and the add c = a + b (2/3 read, "
+                        "1/3 written, the merge's mix) move the same bytes under the same protocol"}
 
 
-def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
-    """fp64 oracle on rank 0's whole share of the workload (every head, forward and backward),
-    repeated until at least ``min_seconds`` of host time have passed; reports the mean rate."""
+def merge_hbm_probe(reps=20):
+    return MergeProbe().run()
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, share, do_bwd, min_seconds=10.0, max_reps=8):
+    """The fp64 oracle on the same rank-0 share, on the host's cores.
+
+    Forward-only workloads (the 32k window): a sample of heads, one head per thread with one
+    BLAS thread each (numpy releases the interpreter lock in its array loops), as many heads
+    as threads; each head rotates q and k at every global position (fp64) and computes the
+    causal attention of the share's rows. Workloads with a backward: every head, forward and
+    backward, numpy's own threading. The rate is the GPU's flop count for the sampled work
+    over the oracle's wall time."""
     import numpy as np
 
     from oracle import attention as oa
+    from oracle import rope as orope
+    t = share.host
+    rows = list(share.pos[0])
+    cores = len(os.sched_getaffinity(0))
+    if not do_bwd:
+        from concurrent.futures import ThreadPoolExecutor
+
+        from threadpoolctl import threadpool_limits
+        n = max(1, min(cores, 16, w.H))
+        heads = list(range(n))
+
+        def one(h):
+            q, k, v = (t[x][:, h:h + 1].double().numpy() for x in ("q", "k", "v"))
+            if w.rope_theta:
+                allpos = np.arange(w.T)
+                q, k = orope.rope_apply(q, allpos, w.rope_theta), orope.rope_apply(k, allpos, w.rope_theta)
+            return oa.causal_attention_fwd(q, k, v, rows=rows)
+
+        t0 = time.perf_counter()
+        with threadpool_limits(1), ThreadPoolExecutor(n) as ex:
+            list(ex.map(one, heads))
+        sec = time.perf_counter() - t0
+        flops = 4 * w.D * share.pairs * w.B * n
+        return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+                "cpu_model": _cpu_model(), "host_cores": cores,
+                "sample": f"rank 0 share of {w.name}, {n} of {w.H} heads (one per thread): "
+                          + ("rotary at every global position, then " if w.rope_theta else "")
+                          + f"causal attention of the share's {len(rows)} rows, forward in fp64 numpy, "
+                            f"{sec:.2f} s",
+                "seconds": sec, "flops": flops}
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = len(os.sched_getaffinity(0))
-    t = share.host
+        threads = cores
     f64 = lambda x: x.double().numpy()
     q, k, v, do = f64(t["q"]), f64(t["k"]), f64(t["v"]), f64(t["do"])
-    rows = list(share.pos[0])
     reps, t0 = 0, time.perf_counter()
     while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         O, L = oa.causal_attention_fwd(q, k, v, rows=rows)
@@ -454,6 +560,7 @@ def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
     sec = (time.perf_counter() - t0) / reps
     flops = share.flops()
     return {"value": flops / sec / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cores": cores,
             "sample": f"rank 0 share of {w.name}, all {w.B * w.H} heads, forward + backward in fp64 numpy, "
                       f"{reps} repetition(s), {sec:.2f} s each", "seconds_per_step": sec}
 
@@ -461,7 +568,8 @@ def cpu_baseline(w, share, min_seconds=10.0, max_reps=8):
 COPY_BYTES = 512 << 20  # calibration copy for the HBM counters (twice the last-level cache)
 # GPU kernels behind each timed launch name (one dispatch of each per launch)
 GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "block_fwd": ("fwd_bf16_kernel",
-               "fwd_rope_kernel"), "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
+               "fwd_rope_kernel"), "block_fwd_merge": ("fwd_bf16_kernel",),
+               "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
                "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",),
                "rope_rotate": ("rope_rotate_kernel",), "rope_rotate_grad": ("rope_rotate_grad_kernel",)}
 
@@ -486,6 +594,15 @@ def kernel_source_hash(kernel="block_bwd"):
     return hsh.hexdigest()[:16]
 
 
+def _calibration_copy():
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def pmc_run(args):
     """A few eager steps of the workload, then the calibration copy three times."""
     import torch
@@ -494,16 +611,26 @@ def pmc_run(args):
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
     share.fused_merge = not args.separate_merge
-    share.build_plan(True)
+    share.build_plan(_do_bwd(args, w))
     for _ in range(3):
         share.step()
     torch.cuda.synchronize()
-    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
+    _calibration_copy()
     print(json.dumps({"pmc_run": w.name, "copy_bytes": COPY_BYTES}))
+
+
+def pmc_merge(args):
+    """Five merges at the 16k-window shape, each after the last-level cache flush, then the
+    calibration copy three times."""
+    import torch
+    p = MergeProbe()
+    for i in range(5):
+        p.flush_cache(i)
+        torch.cuda.synchronize()
+        p.merge()
+        torch.cuda.synchronize()
+    _calibration_copy()
+    print(json.dumps({"pmc_merge": p.rows, "bytes": p.nbytes, "copy_bytes": COPY_BYTES}))
 
 
 def _counter_rows(path):
@@ -518,11 +645,15 @@ def _counter_rows(path):
 
 
 def traffic_from(args):
-    """profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of --pmc-run."""
+    """A traffic file from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of --pmc-run (or
+    --pmc-merge with --traffic-kernel lse_merge)."""
     from workloads import BY_NAME
     w = BY_NAME[args.workload]
-    name = "block_bwd" if not args.split_bwd else "block_bwd_dkdv"
-    out = {"kernel": name, "workload": w.name, "source_hash": kernel_source_hash(name), "copy_bytes": COPY_BYTES,
+    name = args.traffic_kernel or DOMINANT.get(w.name, "block_bwd")
+    if name == "block_bwd" and args.split_bwd:
+        name = "block_bwd_dkdv"
+    out = {"kernel": name, "workload": "merge_hbm_16k" if name == "lse_merge" else w.name,
+           "source_hash": kernel_source_hash(name), "copy_bytes": COPY_BYTES,
            "csv": [os.path.relpath(p, ROOT) for p in args.traffic_from]}
     total = 0.0
     for key, path in zip(("fetch", "write"), args.traffic_from):
@@ -547,12 +678,58 @@ def traffic_from(args):
     print(json.dumps(out))
 
 
+# the launch family with the largest time in each workload's step (the roofline's kernel)
+DOMINANT = {"win32k": "block_fwd", "win16k": "block_fwd", "gpt2s": "block_bwd", "bwd16k": "block_bwd_dkdv",
+            "gqa16k": "block_bwd"}
+
+
+def _do_bwd(args, w):
+    if args.bwd != "auto":
+        return args.bwd == "yes"
+    return not w.rope_theta  # the 32k window with rotary is a forward workload
+
+
+def _traffic_for(kernel, workload):
+    """Measured HBM bytes per launch of a kernel, from the traffic files under profiles/, while
+    they were taken on the kernel's current sources (else None)."""
+    d = os.path.join(ROOT, "profiles")
+    for f in sorted(os.listdir(d)) if os.path.isdir(d) else []:
+        if not (f.startswith("traffic") and f.endswith(".json")):
+            continue
+        try:
+            tj = json.load(open(os.path.join(d, f)))
+        except Exception:
+            continue
+        if tj.get("kernel") == kernel and tj.get("workload") == workload and \
+                tj.get("source_hash") == kernel_source_hash(kernel):
+            return tj.get("bytes_per_launch")
+    return None
+
+
+def _kernels_brief(kern):
+    return {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1), "unit": d["unit"],
+                "frac": round(d["frac"], 4)} for n, d in kern.items()}
+
+
+def _describe(w, do_bwd, fused_merge=True):
+    rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and each K block rotated once, "
+           f"cpattn_rope_rotate)") if w.rope_theta else ""
+    gqa = f", grouped-query ({w.kv_heads} KV heads)" if w.kv_heads != w.H else ""
+    merge = ("LSE merge in the block kernel's epilogue from step 1 on" if fused_merge
+             else "block output then cpattn_lse_merge from step 1 on")
+    parts = f"forward (block fwd; {merge})" + (" and backward (preprocess + dK/dV + dQ)" if do_bwd else "")
+    return (f"{w.name}: rank 0 share of causal ring attention, HeadTail, B={w.B} H={w.H} D={w.D} T={w.T} "
+            f"ring={w.ring}{gqa}{rot}, {parts}, all KV blocks resident")
+
+
 def main():
     args = parse()
     if args.traffic_from:
         return traffic_from(args)
     if args.pmc_run:
         return pmc_run(args)
+    if args.pmc_merge:
+        return pmc_merge(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -560,21 +737,17 @@ def main():
 
     from workloads import BY_NAME
     w = BY_NAME[args.workload]
+    do_bwd = _do_bwd(args, w)
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
     share.fused_merge = not args.separate_merge
-    wall, kern, graphed = time_steps(share, args.steps, args.warmup, graph=not args.no_graph)
-    flops = share.flops()
+    wall, kern, graphed = time_steps(share, args.steps, args.warmup, do_bwd=do_bwd, graph=not args.no_graph)
+    flops = share.flops(do_bwd)
     value = flops / wall / 1e12
-    dom = max(kern, key=lambda n: kern[n]["total_ms"])
-    kd = kern[dom]
-    traffic = None
-    try:
-        tj = json.load(open(args.traffic))
-        if tj.get("kernel") == dom and tj.get("workload") == w.name and tj.get("source_hash") == kernel_source_hash(dom):
-            traffic = tj.get("bytes_per_launch")
-    except Exception:
-        pass
+    fam = EventLog().families(kern)
+    dom = max(fam, key=lambda n: fam[n]["total_ms"])
+    kd = fam[dom]
+    traffic = _traffic_for(dom, w.name)
     line = {
         "metric": "ring-block attention TFLOP/s per GPU (causal-effective) + % bf16 MFMA peak",
         "value": round(value, 2),
@@ -589,34 +762,36 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: rank 0 share of causal ring attention, HeadTail, B={w.B} H={w.H} "
-                               f"D={w.D} T={w.T} ring={w.ring}, forward (block fwd; LSE merge in the block kernel's "
-                               f"epilogue from step 1 on) and backward "
-                               f"(preprocess + dK/dV + dQ), all KV blocks resident",
+        "config": {"workload": _describe(w, do_bwd, share.fused_merge),
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "ring": w.ring, "rank": 0,
+                   "rope_theta": w.rope_theta, "backward": do_bwd,
                    "causal_pairs_per_head": share.pairs, "flops_per_step": flops,
                    "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"kernel": dom, "bound": kd["bound"], "achieved": round(kd["achieved"], 2),
-                     "peak": kd["peak"], "unit": kd["unit"], "frac": round(kd["frac"], 4), "traffic": traffic,
+        "roofline": {"kernel": dom, "launch_names": kd["names"], "bound": kd["bound"],
+                     "achieved": round(kd["achieved"], 2), "peak": kd["peak"], "unit": kd["unit"],
+                     "frac": round(kd["frac"], 4), "traffic": traffic, "launches": kd["launches"],
                      "avg_launch_us": round(kd["avg_us"], 2), "work_per_launch": kd["work_per_launch"]},
         "kernels": {n: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in d.items()}
                     for n, d in kern.items()},
     }
+    fwd_fracs = {w.name: [round(kern[n]["frac"], 4) for n in ("block_fwd", "block_fwd_merge") if n in kern]}
     if not args.no_extra:
         extra = {}
-        for name in ("win16k", "win32k", "gqa16k"):
+        for name in ("win32k", "gpt2s", "win16k", "gqa16k"):
             wx = BY_NAME[name]
+            bwd = True  # the other workloads carry the backward too (the 32k one through rotary)
+            if wx.name == w.name and bwd == do_bwd:
+                continue
             sx = Share(wx, seed_do=wx.seed + 1000)
-            sx.split_bwd = True  # at D = 128 the two halves are separate launches anyway
-            bwd = True
+            sx.split_bwd = wx.D == 128  # at D = 128 the two halves are separate launches anyway
             wl, kx, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=bwd)
             fl = sx.flops(bwd)
-            extra[name] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
-                           "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
-                           "parts": "forward + backward" + (" with rotary" if wx.rope_theta else "") +
-                                    (f" (grouped-query, {wx.kv_heads} KV heads)" if wx.kv_heads != wx.H else ""),
-                           "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
-                                           "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
+            key = name + ("_fwd_bwd" if name == w.name else "")
+            extra[key] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
+                          "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
+                          "parts": _describe(wx, bwd), "kernels": _kernels_brief(kx)}
+            if "block_fwd" in kx and name not in fwd_fracs:
+                fwd_fracs[name] = [round(kx[n]["frac"], 4) for n in ("block_fwd", "block_fwd_merge") if n in kx]
             del sx
             torch.cuda.empty_cache()
         # the 16k window forward with the merge as its own launch (the two-launch form)
@@ -627,29 +802,29 @@ def main():
         fl = sx.flops(False)
         extra["win16k_fwd_two_launch_merge"] = {
             "ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
-            "parts": "forward only, block output then cpattn_lse_merge",
-            "kernels": {n: {"avg_us": round(d["avg_us"], 1), "achieved": round(d["achieved"], 1),
-                            "unit": d["unit"], "frac": round(d["frac"], 4)} for n, d in kx.items()}}
+            "parts": _describe(wx, False, fused_merge=False), "kernels": _kernels_brief(kx)}
         del sx
         torch.cuda.empty_cache()
         extra["merge_hbm_16k"] = merge_hbm_probe()
+        extra["merge_hbm_16k"]["traffic"] = _traffic_for("lse_merge", "merge_hbm_16k")
         line["other_workloads"] = extra
-        # the two throughput targets of the hot path, read off the measurements above:
-        # block forward >= 50 % of the bf16 MFMA peak (16k window, both ring steps), LSE merge
-        # >= 70 % of HBM bandwidth (its own launch in the 16k pipeline, and from HBM with the
-        # last-level cache flushed)
-        k16 = extra["win16k"]["kernels"]
-        fwd_fracs = [k16[n]["frac"] for n in ("block_fwd", "block_fwd_merge") if n in k16]
+        # the two throughput targets of the hot path: block forward >= 50 % of the bf16 MFMA
+        # peak on both ring steps (32k and 16k windows), LSE merge >= 70 % of HBM bandwidth read
+        # from HBM (cache flushed); the merge's launch inside the 16k pipeline finds part of its
+        # operands in the last-level cache and is reported beside it, not as the target
         mrg = extra["win16k_fwd_two_launch_merge"]["kernels"].get("lse_merge", {})
+        mh = extra["merge_hbm_16k"]
         line["targets"] = {
-            "block_fwd_bf16_peak": {"target": 0.5, "workload": "win16k", "frac_per_step": fwd_fracs,
-                                    "met": bool(fwd_fracs) and min(fwd_fracs) >= 0.5},
-            "lse_merge_hbm": {"target": 0.7, "frac_in_pipeline": mrg.get("frac"),
-                              "frac_cache_flushed": round(extra["merge_hbm_16k"]["frac_hbm"], 4),
-                              "met_in_pipeline": mrg.get("frac", 0.0) >= 0.7},
+            "block_fwd_bf16_peak": {"target": 0.5, "frac_per_step": fwd_fracs,
+                                    "met": all(f and min(f) >= 0.5 for f in fwd_fracs.values())},
+            "lse_merge_hbm": {"target": 0.7, "frac_cache_flushed": round(mh["frac_hbm"], 4),
+                              "frac_of_stream_2to1": round(mh["frac_of_stream_2to1"], 4),
+                              "stream_2to1_frac_hbm": round(mh["stream_2to1_GB/s"] / PEAK_HBM_GBS, 4),
+                              "frac_in_pipeline_cache_assisted": mrg.get("frac"),
+                              "met": mh["frac_hbm"] >= 0.7},
         }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, share)
+        line["cpu_baseline"] = cpu_baseline(w, share, do_bwd)
     print(json.dumps(line))
 
 
