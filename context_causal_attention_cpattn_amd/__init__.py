@@ -25,7 +25,7 @@ __all__ = [
     "cpattn_ring_fwd_workspace_bytes",
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
     "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
-    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "EXPORTS",
+    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc", "NOALLOC_MAX_ROWS", "EXPORTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,8 +38,10 @@ EXPORTS = (
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
     "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
-    "cpattn_ring_bwd", "cpattn_block_fwd_merge",
+    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc",
 )
+
+NOALLOC_MAX_ROWS = 1 << 20  # CPATTN_NOALLOC_MAX_ROWS: B*H*Tq limit of cpattn_ring_bwd_noalloc
 
 
 class CpattnError(RuntimeError):
@@ -90,6 +92,8 @@ _SIGS = {
     "cpattn_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "cpattn_ring_bwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _T, _T, _T, _T, _T, _T, _i32, _vp, ctypes.c_size_t, _vp]),
+    "cpattn_ring_bwd_noalloc": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64,
+                                               _i32, _f32, _T, _T, _T, _T, _T, _T, _i32, _vp]),
 }
 
 _lib = None
@@ -354,6 +358,36 @@ def cpattn_ring_bwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, 
     _check(load().cpattn_ring_bwd(_tensor(q), ks, vs, ms, n, rank, _map(qmap), _dtype(q), B, H, Tq, Tk, D,
                                   int(causal), float(scale), _tensor(dout), _tensor(o), _tensor(lse, 3),
                                   _tensor(dq_acc), dks, dvs, int(accumulate), ws, wsb, _stream(stream)))
+
+
+def cpattn_ring_bwd_noalloc(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, dout, o,
+                            lse, dq_acc, dk_blocks: Sequence, dv_blocks: Sequence, causal: bool = True,
+                            scale: float = 0.0, accumulate: bool = True, stream=None):
+    """cpattn_ring_bwd with its fp32 delta in the library's static device array instead of a caller
+    workspace (B*H*Tq <= NOALLOC_MAX_ROWS); allocates nothing. Calls that overlap on one GPU race."""
+    n = len(k_blocks)
+    if len(v_blocks) != n or len(kmaps) != n or len(dk_blocks) != n or len(dv_blocks) != n:
+        raise ValueError("k_blocks, v_blocks, kmaps, dk_blocks, dv_blocks must have the same length")
+    if n < 1:
+        raise ValueError("at least one KV block is needed")
+    B, H, _, Tq, Tk, D = _inputs(q, k_blocks[0], v_blocks[0], q.shape[1] if q is not None and q.dim() == 4 else None)
+    for i in range(n):
+        _expect(f"k_blocks[{i}]", k_blocks[i], (B, H, Tk, D), q.dtype, q)
+        _expect(f"v_blocks[{i}]", v_blocks[i], (B, H, Tk, D), q.dtype, q)
+        _expect(f"dk_blocks[{i}]", dk_blocks[i], (B, H, Tk, D), _f32(), q)
+        _expect(f"dv_blocks[{i}]", dv_blocks[i], (B, H, Tk, D), _f32(), q)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("o", o, (B, H, Tq, D), _f32(), q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
+    ks = (cpattn_tensor * n)(*[_tensor(t) for t in k_blocks])
+    vs = (cpattn_tensor * n)(*[_tensor(t) for t in v_blocks])
+    dks = (cpattn_tensor * n)(*[_tensor(t) for t in dk_blocks])
+    dvs = (cpattn_tensor * n)(*[_tensor(t) for t in dv_blocks])
+    ms = (cpattn_posmap * n)(*[_map(m) for m in kmaps])
+    _check(load().cpattn_ring_bwd_noalloc(_tensor(q), ks, vs, ms, n, rank, _map(qmap), _dtype(q), B, H, Tq, Tk, D,
+                                          int(causal), float(scale), _tensor(dout), _tensor(o), _tensor(lse, 3),
+                                          _tensor(dq_acc), dks, dvs, int(accumulate), _stream(stream)))
 
 
 def cpattn_bwd_preprocess(dout, o, delta, stream=None):

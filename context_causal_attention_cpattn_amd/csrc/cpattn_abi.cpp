@@ -31,6 +31,18 @@ int ok() {
   return CPATTN_OK;
 }
 
+}  // namespace
+
+int cpattn::api_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+namespace {
+
 constexpr int64_t kIntMax = 2147483647;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }

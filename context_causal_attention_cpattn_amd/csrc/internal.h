@@ -101,4 +101,9 @@ struct RotGradArgs {
 };
 hipError_t launch_rope_rotate_grad(const RotGradArgs& a, hipStream_t s);
 
+// Records `code` and a printf-style message as the thread's last error (what
+// cpattn_last_error returns) and returns `code`; for entry points defined
+// outside cpattn_abi.cpp.
+int api_fail(int code, const char* fmt, ...);
+
 }  // namespace cpattn

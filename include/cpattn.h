@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 5
+#define CPATTN_ABI_VERSION 6
 
 enum {
   CPATTN_OK = 0,
@@ -386,6 +386,33 @@ int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks,
                     const cpattn_tensor* lse, const cpattn_tensor* dq_acc,
                     const cpattn_tensor* dk_blocks, const cpattn_tensor* dv_blocks,
                     int32_t accumulate, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * cpattn_ring_bwd without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, semantics, launches and results as
+ * cpattn_ring_bwd, bit for bit; the fp32 delta of the local rows lives in a
+ * static device array of CPATTN_NOALLOC_MAX_ROWS floats (4 MiB) that each GPU
+ * the library runs on holds until the process ends. Its address is looked up
+ * on the first call made with a device current (call once outside graph
+ * capture before capturing); the stream must belong to the current device.
+ * The call allocates nothing and frees nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or threads without ordering) race and give wrong
+ * results; calls ordered on one stream are safe. Nothing in the array needs to
+ * start at zero (every row of delta is written before it is read).
+ * Errors: as cpattn_ring_bwd, plus EINVAL if B*H*Tq > CPATTN_NOALLOC_MAX_ROWS
+ * (checked before any launch) and EHIP if the array's address cannot be found.
+ */
+#define CPATTN_NOALLOC_MAX_ROWS (1 << 20)
+int cpattn_ring_bwd_noalloc(const cpattn_tensor* q, const cpattn_tensor* k_blocks,
+                            const cpattn_tensor* v_blocks, const cpattn_posmap* kmaps,
+                            int32_t ring, int32_t rank, const cpattn_posmap* qmap, int32_t dtype,
+                            int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t causal,
+                            float scale, const cpattn_tensor* dout, const cpattn_tensor* o,
+                            const cpattn_tensor* lse, const cpattn_tensor* dq_acc,
+                            const cpattn_tensor* dk_blocks, const cpattn_tensor* dv_blocks,
+                            int32_t accumulate, void* stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 5
+    assert cp.cpattn_version() == 6
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -292,3 +292,15 @@ def test_gqa_rejects_group_mismatch():
                                                    H, H_kv, 64, 64, 64, bm, bm, 1, 0.0, 1, None)
     assert bwd(6, 4) == -1
     assert bwd(3, -1) == -1
+
+
+def test_ring_bwd_noalloc_rejects_more_rows_than_its_scratch():
+    # checked before any device query or launch: B*H*Tq above the static array's rows
+    lib = cp.load()
+    m = cp.cpattn_posmap(4, 4, 0, 0)
+    nil = ctypes.POINTER(cp.cpattn_tensor)()
+    rows = cp.NOALLOC_MAX_ROWS
+    for B, H, Tq in ((1, 1, rows + 8), (2, 8, rows // 8), (rows, 2, 1)):
+        st = lib.cpattn_ring_bwd_noalloc(nil, nil, nil, ctypes.byref(m), 1, 0, ctypes.byref(m), 1, B, H, Tq, 4, 64, 1,
+                                         0.0, nil, nil, nil, nil, nil, nil, 1, None)
+        assert st == -1 and "static scratch" in cp.cpattn_last_error()
