@@ -6,11 +6,12 @@ The default workload is rank 0 of the 32k window with rotary (B=1, H=16,
 D=128, T=32768, ring degree 2; bf16 inputs, fp32 accumulation), every KV block
 resident in HBM:
 
-  * Q rotated once at its global positions (cpattn_rope_rotate);
-  * for each ring step s (block owner src = -s mod 2): the block's keys rotated
-    at the owner's positions, then the block forward of the visible rows --
-    step 0 straight into the running (O, LSE), step 1 with the LSE merge in the
-    block kernel's epilogue (cpattn_block_fwd_merge).
+  * Q and the rank's own K block rotated once at their global positions
+    (cpattn_rope_rotate); the other rank's block arrives rotated (its owner
+    rotated it once, outside this rank's step, before sending it);
+  * for each ring step s (block owner src = -s mod 2): the block forward of the
+    visible rows -- step 0 straight into the running (O, LSE), step 1 with the
+    LSE merge in the block kernel's epilogue (cpattn_block_fwd_merge).
 
 ``--workload gpt2s`` (and the other workloads) time their own steps; those with
 a backward add the preprocess and one block backward per ring step.
@@ -113,12 +114,16 @@ class Share:
         Tl = w.local_len
         self.tab = None
         if w.rope_theta:
-            # rotary: Q is rotated once per step and each K block once per ring step
-            # (cpattn_rope_rotate), then the blocks run without rotation
+            # rotary: every rank rotates its Q and its own K block once per step
+            # (cpattn_rope_rotate) and sends the rotated block; the blocks then run without
+            # rotation. The other ranks' blocks are rotated here, outside rank 0's step, as
+            # their owners would before sending them.
             self.tab = torch.empty(w.T, w.D, device=dev)
             cp.cpattn_rope_table(w.rope_theta, w.T, w.D, self.tab)
             self.q_rot = torch.empty_like(self.q)
-            self.k_rot = torch.empty_like(self.kb[0])
+            self.k_rot = [torch.empty_like(x) for x in self.kb]
+            for r in range(1, N):
+                cp.cpattn_rope_rotate(self.kb[r], self.maps[r], self.tab, out=self.k_rot[r])
         f32 = dict(device=dev, dtype=torch.float32)
         self.o = torch.empty(w.B, w.H, Tl, w.D, **f32)
         self.lse = torch.empty(w.B, w.H, Tl, **f32)
@@ -177,21 +182,24 @@ class Share:
         qf = q
         if self.tab is not None:
             tab, rows = cp.ctypes.c_void_p(self.tab.data_ptr()), self.tab.shape[0]
-            qf, kr = T(self.q_rot), T(self.k_rot)
-            keep += [qf, kr]
+            qf = T(self.q_rot)
+            kr = [T(x) for x in self.k_rot]
+            keep += [qf] + kr
             # x read + out written (bf16), the table row of each position once
             rot_bytes = B * H * Tl * 4 * D + Tl * 4 * D
+            k0, km0 = T(self.kb[0]), cp._map(self.maps[0])
+            keep += [k0, km0]
             plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
                          (by(q), bf16, B, H, Tl, D, by(qm), tab, rows, by(qf), st)))
+            plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
+                         (by(k0), bf16, B, H, Tk, D, by(km0), tab, rows, by(kr[0]), st)))
         for s, (src, rb, pairs) in enumerate(self.steps):
             if rb >= Tl:
                 continue
             k, v, km = T(self.kb[src]), T(self.vb[src]), cp._map(self.maps[src])
             keep += [k, v, km]
             if self.tab is not None:
-                plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
-                             (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
-                k = kr
+                k = kr[src]  # rotated once by its owner
             if s > 0 and self.fused_merge:
                 plan.append(("block_fwd_merge", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_merge,
                              (by(qf), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, rb, Tl,
@@ -220,10 +228,8 @@ class Share:
                 dk, dv = T(self.dk[src]), T(self.dv[src])
                 keep += [k, v, km, dk, dv]
                 if self.tab is not None:
-                    # backward over the rotated rows: rotate the block's keys again, Q stays rotated
-                    plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
-                                 (by(k), bf16, B, H, Tk, D, by(km), tab, rows, by(kr), st)))
-                    k, q = kr, qf
+                    # backward over the rotated rows kept from the forward
+                    k, q = kr[src], qf
                 if gqa:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd_gqa,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
@@ -234,25 +240,26 @@ class Share:
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
                                   B, H, Tl, Tk, D, by(qm), by(km), 1, 0.0, acc, st)))
                     continue
-                plan.append(("block_bwd_dkdv", 8 * D * pairs * self.bh, lib.cpattn_block_bwd_dkdv,
+                # the 10*D flops per pair of the backward, split between the halves: each gets the
+                # products only it needs (dV and dK: 4*D; dQ: 2*D) and half of the S and dP
+                # recompute both form (2*D each), so the halves sum to the whole
+                plan.append(("block_bwd_dkdv", 6 * D * pairs * self.bh, lib.cpattn_block_bwd_dkdv,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dk), by(dv), B, H, Tl, Tk, D,
                               by(qm), by(km), 1, 0.0, acc, st)))
-                plan.append(("block_bwd_dq", 6 * D * pairs * self.bh, lib.cpattn_block_bwd_dq,
+                plan.append(("block_bwd_dq", 4 * D * pairs * self.bh, lib.cpattn_block_bwd_dq,
                              (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), B, H, Tl, Tk, D, by(qm),
                               by(km), 1, 0.0, acc, st)))
             if self.tab is not None:
-                # gradients back through R^T once: dQ, then every dK block (fp32 read and written,
-                # the table row of each position once)
+                # gradients back through R^T once: dQ and the own block's dK (fp32 read and
+                # written, the table row of each position once). The other blocks' dK partials
+                # travel back to their owners, which apply R^T to their summed dK.
                 gbytes = B * H * Tl * 8 * D + Tl * 4 * D
                 plan.append(("rope_rotate_grad", gbytes, lib.cpattn_rope_rotate_grad,
                              (by(dq), B, H, Tl, D, by(qm), tab, rows, st)))
-                for src, rb, _ in self.steps:
-                    if rb >= Tl:
-                        continue
-                    dk, km = T(self.dk[src]), cp._map(self.maps[src])
-                    keep += [dk, km]
-                    plan.append(("rope_rotate_grad", gbytes, lib.cpattn_rope_rotate_grad,
-                                 (by(dk), B, H, Tk, D, by(km), tab, rows, st)))
+                dk0, km0 = T(self.dk[0]), cp._map(self.maps[0])
+                keep += [dk0, km0]
+                plan.append(("rope_rotate_grad", gbytes, lib.cpattn_rope_rotate_grad,
+                             (by(dk0), B, H, Tk, D, by(km0), tab, rows, st)))
         self._keep = keep
         self.plan = plan
         self.do_bwd = do_bwd
@@ -459,11 +466,14 @@ class MergeProbe:
         self.cp.cpattn_lse_merge(self.o_acc, self.l_acc, self.o_blk, self.l_blk, self.rb, self.T)
 
     def median_us(self, fn, reps=20):
+        """Median launch time over ``reps`` launches, each after a cache flush. The flush is
+        still running on the GPU while the host queues the timed launch, so the events
+        bracket the kernel alone, not the host's time to marshal and submit it."""
         import torch
         times = []
         for i in range(reps + 3):
-            self.flush_cache(i)
             torch.cuda.synchronize()
+            self.flush_cache(i)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -712,8 +722,8 @@ def _kernels_brief(kern):
 
 
 def _describe(w, do_bwd, fused_merge=True):
-    rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and each K block rotated once, "
-           f"cpattn_rope_rotate)") if w.rope_theta else ""
+    rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and the own K block rotated once per "
+           f"step with cpattn_rope_rotate; the other block arrives rotated by its owner)") if w.rope_theta else ""
     gqa = f", grouped-query ({w.kv_heads} KV heads)" if w.kv_heads != w.H else ""
     merge = ("LSE merge in the block kernel's epilogue from step 1 on" if fused_merge
              else "block output then cpattn_lse_merge from step 1 on")

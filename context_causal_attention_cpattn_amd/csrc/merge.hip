@@ -20,9 +20,11 @@ namespace {
 // values and the weights are formed once per thread, and the NV loads of each operand
 // are issued together before any arithmetic. Both O operands are read with
 // non-temporal loads (each byte is read once; the result is written in place).
+constexpr int kMergeNV = 2;  // float4 per thread
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_thr) {
-  constexpr int NV = 4;             // float4 per thread
+  constexpr int NV = kMergeNV;
   constexpr int TPR = D / 4 / NV;   // threads per row
   const int rows = a.row_end - a.row_begin;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a, int64_t n_thr) 
 template <int D>
 hipError_t merge_d(const MergeArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * (a.row_end - a.row_begin);
-  const int64_t n_thr = rows * (D / 16);
+  const int64_t n_thr = rows * (D / 4 / kMergeNV);
   if (n_thr <= 0) return hipSuccess;
   int64_t blocks = (n_thr + 255) / 256;
   const int64_t cap = 256 * 64;  // 64 workgroups per CU at most; the loop covers the rest
