@@ -1,38 +1,18 @@
-// Block forward with fused rotary position embedding, bf16 inputs, fp32
-// accumulation, MFMA (gfx950).
+// Block forward with fused rotary position embedding (the table form of
+// cpattn_block_fwd), bf16 inputs, fp32 accumulation, MFMA (gfx950).
 //
-// Computes, for the local query rows of one ring step against one KV block at
-// global positions, the partial output O and its log-sum-exp (BluScriptCP
-// development log: 2026-04-20 CP-aware attention with separate query/key
-// lengths and offsets; 2026-06-29 requirements: dual-offset global-causal
-// mask, log-sum-exp as an output; 2026-07-10: positions through head/tail
-// deltas).
-//
-// Work decomposition
-//   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
-//     rows for the whole kernel and keeps them in registers;
-//   * K and V tiles of 64 keys are staged through LDS, double buffered. They
-//     are loaded with global_load_lds_dwordx4 (16 bytes per lane straight into
-//     LDS, no register staging) into an unpadded, XOR-swizzled layout that is
-//     free of bank conflicts both for the 16-byte row reads of the K operand and
-//     for the transposing reads of the V^T operand;
-//   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
-//     so every lane holds 16 scores of ONE query row per 32-key block: the row
-//     max is an in-lane max3 chain plus one exchange with lane l^32, and the row
-//     sum stays a per-lane partial until the epilogue;
-//   * the output is accumulated transposed, O^T += V^T P^T: P comes straight
-//     from the score registers (same lane = same query), and V^T is read from
-//     the row-major V tile with the transposing LDS read (ds_read_b64_tr_b16);
-//   * the causal mask is tested only on tiles that straddle the diagonal in
-//     global positions; tiles past the last visible key are never loaded;
-//   * the softmax max is rescaled lazily: the running max moves only when a new
-//     score exceeds it by more than 2^8, so the accumulator is rarely rescaled
-//     (exact: O and the row sum always share the same reference max);
-//   * workgroup ids are remapped so that the query tiles of one (b, h) run on
-//     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first.
-//   * with rotary embedding, K is staged through registers instead (it must be
-//     rotated at its global position before it reaches LDS); Q is rotated once
-//     in the prologue.
+// The same block attention as fwd_bf16.hip (partial O and log-sum-exp of the
+// local query rows against one KV block at global positions; BluScriptCP
+// development log, 2026-04-20 and 2026-06-29), with the rotary embedding of
+// 2026-06-29 / 2026-07-10 applied inside the kernel at each row's global
+// position: Q is rotated once in the prologue; K is staged through registers
+// and rotated on its way to LDS (V still goes global -> LDS directly). Work
+// split, LDS layout, score/output transposition, masking, lazy rescale and
+// workgroup order are those of fwd_bf16.hip; the loop here is not software
+// pipelined (the K rotation sits between the tile load and the barrier).
+// The ring driver instead rotates Q and each K block once (cpattn_rope_rotate)
+// and runs the plain kernel, which is faster when a block meets many query
+// tiles; this form needs no workspace.
 
 #include "internal.h"
 
@@ -61,11 +41,10 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p;
 
 // K is staged through registers (rotated at its global position on the way to
 // LDS), V with direct loads; both double buffered.
-template <int D, bool ROPE, int NS>
+template <int D>
 __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
-  static_assert(!ROPE || NS == 2, "rotary variant is double buffered");
-  static_assert(NS >= 2 && NS <= 4, "pipeline depth");
+  constexpr int NS = 2;
   __shared__ __attribute__((aligned(1024))) char smem[NS][2][C::TILEB];  // [stage][K,V]
 
   const int tid = threadIdx.x;
@@ -94,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
     qf[c] = __builtin_bit_cast(bf16x8, t);
   }
   const int qpos = a.qm.pos(row_ok ? row : a.row_end - 1);
-  if constexpr (ROPE) {
+  {
     if (row_ok) {
       const float* tb = a.rope + (int64_t)qpos * D;
 #pragma unroll
@@ -153,15 +132,14 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
         k_off = (unsigned)((r * a.k.st + ld_col[i]) * 2);
         v_off = (unsigned)((r * a.v.st + ld_col[i]) * 2);
       }
-      if constexpr (!ROPE) load_lds16(kbase, k_off, smem[buf][0] + (w * C::NI + i) * 1024);
       load_lds16(vbase, v_off, smem[buf][1] + (w * C::NI + i) * 1024);
     }
   };
   // rotary: K chunk pairs (c, c + D/2) of a row through registers
-  u32x4 kr[ROPE ? 2 * C::PPT : 1];
-  f32x4 tr[ROPE ? 4 * C::PPT : 1];
+  u32x4 kr[2 * C::PPT];
+  f32x4 tr[4 * C::PPT];
   auto load_k_regs = [&](int kt) {
-    if constexpr (ROPE) {
+    {
 #pragma unroll
       for (int i = 0; i < C::PPT; ++i) {
         const int p = tid + 64 * kNW * i;
@@ -178,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
     }
   };
   auto store_k_regs = [&](int buf) {
-    if constexpr (ROPE) {
+    {
       char* ks = smem[buf][0];
 #pragma unroll
       for (int i = 0; i < C::PPT; ++i) {
@@ -241,10 +219,7 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int cur = kt % NS;
-    // tile kt has landed for this wave once only the tiles issued after it are outstanding
-    const int later = min(NS - 2, n_kt - 1 - kt);
-    if constexpr (ROPE) wait_vm0();
-    else wait_tiles<(ROPE ? 1 : 2) * C::NI>(later);
+    wait_vm0();  // the K registers of tile kt+1 are loaded each iteration: wait for everything
     __syncthreads();  // tile kt visible to every wave; every wave is done with tile kt-1's stage
     if (kt + NS - 1 < n_kt) {
       issue_tile(kt + NS - 1, (kt + NS - 1) % NS);
@@ -356,7 +331,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int n_qt = (rows + kBM - 1) / kBM;
   const int64_t grid = (int64_t)n_qt * a.B * a.H;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_rope_kernel<D, true, 2>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
+  hipLaunchKernelGGL((fwd_rope_kernel<D>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, a, n_qt);
   return hipGetLastError();
 }
 
