@@ -8,13 +8,17 @@
 // deltas).
 //
 // Work decomposition
-//   * one workgroup = 4 waves = 128 query rows of one (b, h); each wave owns 32
-//     rows for the whole kernel and keeps them in registers;
+//   * one workgroup = 4 waves = 128 query rows of one (b, h) at D = 64 (two
+//     workgroups per CU), 8 waves = 256 rows at D = 128 (one per CU); each wave
+//     owns 32 rows for the whole kernel and keeps them in registers;
 //   * K and V tiles of 64 keys are staged through LDS, double buffered. They
 //     are loaded with global_load_lds_dwordx4 (16 bytes per lane straight into
 //     LDS, no register staging) into an unpadded, XOR-swizzled layout that is
 //     free of bank conflicts both for the 16-byte row reads of the K operand and
-//     for the transposing reads of the V^T operand;
+//     for the transposing reads of the V^T operand. At D = 128 only waves 4..7
+//     issue the tile loads: waves 0..3 enter their matrix work straight after
+//     the barrier while the loaders queue 32 KB per tile in the address unit,
+//     and the K/V bytes loaded per flop are half those of two 4-wave workgroups;
 //   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
 //     so every lane holds 16 scores of ONE query row per 32-key block: the row
 //     max is an in-lane max3 chain plus one exchange with lane l^32, and the row
@@ -40,8 +44,8 @@
 namespace cpattn {
 namespace {
 
-constexpr int kNW = 4;          // waves per workgroup
-constexpr int kBM = 32 * kNW;   // query rows per workgroup
+constexpr int kNW = 4;          // waves per workgroup at D = 64
+constexpr int kBM = 32 * kNW;   // query rows per workgroup at D = 64
 constexpr int kBN = 64;         // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units
 
@@ -50,7 +54,6 @@ struct Cfg {
   static constexpr int ROWB = D * 2;              // bytes per tile row (no padding)
   static constexpr int CPR = D / 8;               // 16-byte chunks per row
   static constexpr int TILEB = kBN * ROWB;        // bytes per K or V tile
-  static constexpr int NI = kBN * CPR / (64 * kNW);  // direct loads per wave per tile
   static constexpr int NC = D / 16;               // 16-wide k-chunks of D
   static constexpr int NDB = D / 32;              // 32-row blocks of D in O^T
   __device__ static __forceinline__ int mask(int r) { return swz_mask<D>(r); }
@@ -87,12 +90,15 @@ __device__ __forceinline__ void wait_units(int units) {
 // results (accumulator, reference max, row sum) are merged into the even pair's
 // through LDS. A workgroup then covers 64 rows, so a step has twice as many
 // workgroups, each walking half the keys.
-template <int D, int NS, int KS>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
+//
+// NW is the number of waves of a workgroup (4: two workgroups per CU, 8: one).
+// With SPLIT_LOAD only the upper half of a key share's waves issue its tile loads.
+template <int D, int NS, int KS, int NW, bool SPLIT_LOAD>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   using C = Cfg<D>;
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
   static_assert(KS == 1 || (KS == 2 && D == 64), "key split: 64-wide heads only");
-  constexpr int NR = kNW / KS;     // waves per key share (one 32-row block each)
+  constexpr int NR = NW / KS;      // waves per key share (one 32-row block each)
   constexpr int ROWS = 32 * NR;    // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) char ksm[KS][NS][C::TILEB];
   __shared__ __attribute__((aligned(1024))) char vsm[KS][NS][C::TILEB];
@@ -144,30 +150,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
   const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
 
-  // ---- direct global -> LDS loads: the NR waves of a key share fill the 1 KB slots of that
-  // share's tiles, wave rb the slots rb + NR*i (i < NIH). Slot position p = 64*slot + lane is
-  // tile row p / CPR, physical chunk p % CPR. The rows of a lane's slots differ by
-  // 64*NR/CPR, a multiple of the swizzle period, so the lane's byte offset is the same for
-  // all of them and only the (scalar) row base moves.
-  constexpr int NIH = C::NI * KS;                // loads per wave per tile
-  constexpr int kSlotRows = 64 * NR / C::CPR;  // rows between a lane's consecutive slots
-  const int ld_r0 = (64 * rb + l) / C::CPR;
+  // ---- direct global -> LDS loads: the NL loader waves of a key share fill the 1 KB slots
+  // of that share's tiles, loader lw the slots lw + NL*i (i < NIH). Slot position
+  // p = 64*slot + lane is tile row p / CPR, physical chunk p % CPR. The rows of a lane's
+  // slots differ by 64*NL/CPR, a multiple of the swizzle period, so the lane's byte offset
+  // is the same for all of them and only the (scalar) row base moves.
+  constexpr int NL = SPLIT_LOAD ? NR / 2 : NR;    // loader waves per key share
+  const bool loader = rb >= NR - NL;              // wave-uniform
+  const int lw = rb - (NR - NL);                  // loader index
+  constexpr int NIH = kBN * C::CPR / (64 * NL);  // loads per loader wave per tile
+  constexpr int kSlotRows = 64 * NL / C::CPR;  // rows between a lane's consecutive slots
+  const int ld_r0 = (64 * lw + l) / C::CPR;
   const int ld_col = ((l % C::CPR) ^ C::mask(ld_r0)) * 8;
   const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
   const unsigned vo = (unsigned)((ld_r0 * a.v.st + ld_col) * 2);
   // rows past the block repeat the last key (masked later)
   static_assert(kSlotRows % 16 == 0, "slot rows must be a multiple of the swizzle period");
   auto issue = [&](const __bf16* base, int64_t st, unsigned off, int kt, char* dst) {
+    if (!loader) return;
     const char* tb = (const char*)(base + (int64_t)kt * kBN * st);
     if (kt * kBN + kBN <= a.Tk) {
 #pragma unroll
       for (int i = 0; i < NIH; ++i)
-        load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (rb + NR * i) * 1024);
+        load_lds16(tb + (int64_t)kSlotRows * i * st * 2, off, dst + (lw + NL * i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < NIH; ++i) {
         const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - kt * kBN);
-        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (rb + NR * i) * 1024);
+        load_lds16(tb, (unsigned)((r * st + ld_col) * 2), dst + (lw + NL * i) * 1024);
       }
     }
   };
@@ -479,20 +489,26 @@ template <int D>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
   const int64_t bh = (int64_t)a.B * a.H;
-  const int64_t grid1 = (int64_t)((rows + kBM - 1) / kBM) * bh;
-  if (grid1 <= 0) return hipSuccess;
-  if constexpr (D == 64) {
+  if (rows <= 0 || bh <= 0) return hipSuccess;
+  if constexpr (D == 128) {
+    constexpr int NW = 8;
+    const int n_qt = (rows + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1, NW, true>), dim3((unsigned)(n_qt * bh)), dim3(64 * NW), 0, s, a,
+                       n_qt);
+    return hipGetLastError();
+  } else {
+    const int64_t grid1 = (int64_t)((rows + kBM - 1) / kBM) * bh;
     // fewer than two workgroups per CU: split each workgroup's keys between two wave pairs
     if (grid1 < 512) {
       const int n_qt = (rows + kBM / 2 - 1) / (kBM / 2);
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s, a, n_qt);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2, kNW, false>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s,
+                         a, n_qt);
       return hipGetLastError();
     }
+    const int n_qt = (rows + kBM - 1) / kBM;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1, kNW, false>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt);
+    return hipGetLastError();
   }
-  constexpr int NS = D == 64 ? 4 : 2;
-  const int n_qt = (rows + kBM - 1) / kBM;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NS, 1>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt);
-  return hipGetLastError();
 }
 
 }  // namespace
