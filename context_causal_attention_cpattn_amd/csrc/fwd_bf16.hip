@@ -286,6 +286,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
     __syncthreads();  // group j visible to its share; every wave is done with V_j-1 and K_j
     issue_group(j + NS - 1);
 
+    // The two waves of a SIMD belong to one 8-wave workgroup and would otherwise run their
+    // tiles in step; a wave forming the next scores takes issue priority over one in its
+    // PV products, which staggers them.
+    if constexpr (NW == 8) __builtin_amdgcn_s_setprio(1);
     // ---- lazy rescale: the running max moves only when a score exceeds it by 2^8
     const float m_tile = mx * sl2;
     const bool need = m_tile > m_run + kRescaleSlack;
@@ -335,6 +339,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
       if constexpr (NEXT) sn[kb] = acc_s;
     }
 
+    if constexpr (NW == 8) __builtin_amdgcn_s_setprio(0);
     // ---- phase B: O^T += V^T P^T (V^T rows = d, 8 keys 16t + 4h + {0..3}, +8), while the
     // vector ALUs take the row max of S_kt+1. V^T operands are read one MFMA ahead.
     constexpr int EB = 32 / (4 * C::NDB);  // score elements per MFMA slot
