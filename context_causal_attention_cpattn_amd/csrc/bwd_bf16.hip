@@ -8,12 +8,14 @@
 //   P  = exp(sigma q k^T - LSE)        (visible pairs only)
 //   dV += P^T dO,  dS = P * (dO v^T - delta),  dQ += sigma dS k,  dK += sigma dS^T q.
 //
-// Two kernels, no atomics (bitwise reproducible):
-//   * dkdv: a workgroup owns 128 keys (32 per wave, kept in registers with
-//     their V rows) and walks the query tiles that can see them. Scores are
-//     formed as S = Q K^T so every lane holds one key; P^T and dS^T then feed
-//     the A operand of dV += P^T dO and dK += dS^T Q straight from registers,
-//     and dO / Q enter as B operands through the transposing LDS read.
+// Two halves, no atomics (bitwise reproducible):
+//   * dkdv: a workgroup owns 128 keys and walks the query tiles that can see
+//     them. Scores are formed as S = Q K^T so every lane holds one key; P^T
+//     and dS^T then feed the A operand of dV += P^T dO and dK += dS^T Q
+//     straight from registers, and dO / Q enter as B operands through the
+//     transposing LDS read. At D = 64 each of 4 waves owns 32 keys with both
+//     accumulators; at D = 128 two waves share 32 keys, one forming P and dV,
+//     the other dP, dS and dK (8 waves, P handed over through LDS).
 //   * dq: a workgroup owns 128 query rows and walks the visible key tiles, like
 //     the forward: S^T = K Q^T and dP^T = V dO^T give one query per lane, and
 //     dQ^T += K^T dS^T reads K^T with the transposing LDS read.
@@ -81,13 +83,10 @@ struct DkdvLds {
   alignas(16) float sdelta[NS][kTile];
 };
 
-// Workgroup Lg of the dK/dV grid (Lg = bh * n_kt + key tile).
-// PART selects what one launch forms: 0 both dK and dV, 1 dV only (no V rows, no dP),
-// 2 dK only. A launch of one part keeps one accumulator, which brings the 128-wide
-// kernel within two waves per SIMD at the price of forming S in both launches.
-template <int D, int NS, int PART>
+// Workgroup Lg of the dK/dV grid (Lg = bh * n_kt + key tile); 64-wide heads.
+template <int D, int NS>
 __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, DkdvLds<D, NS>& sm) {
-  constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
+  static_assert(D == 64, "128-wide heads take dkdv_pair_body");
   using C = BCfg<D>;
   auto& sq = sm.sq;
   auto& sdo = sm.sdo;
@@ -186,7 +185,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     for (int c = 0; c < C::NC; ++c) {
       u32x4 z = {0u, 0u, 0u, 0u};
       kf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(kk + 16 * c + 8 * h) : z);
-      if constexpr (WANT_DK) vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
+      vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
     }
   }
   // Complete the register loads before the tile loop, so that the compiler's wait for them
@@ -195,7 +194,7 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 #pragma unroll
   for (int c = 0; c < C::NC; ++c) {
     asm volatile("" ::"v"(kf[c]));
-    if constexpr (WANT_DK) asm volatile("" ::"v"(vf[c]));
+    asm volatile("" ::"v"(vf[c]));
   }
 
   // every query head of the group in turn: dK and dV sum over the group in registers
@@ -213,41 +212,24 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
     for (int qb = 0; qb < 2; ++qb) {
       // operands of S = Q K^T and dP = dO V^T for 32 query rows, read as one batch
       f32x16 s = f32x16{}, dpv = f32x16{};
-      if constexpr (PART != 2) {
-        bf16x8 qa[C::NC], da[C::NC];
+      bf16x8 qa[C::NC], da[C::NC];
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          qa[c] = *(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]);
-          if constexpr (WANT_DK) da[c] = *(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < C::NC; ++c) {
+        qa[c] = *(const bf16x8*)(Q + 32 * qb * C::ROWB + off.ro[c]);
+        da[c] = *(const bf16x8*)(DO + 32 * qb * C::ROWB + off.ro[c]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < C::NC; ++c) {
-          s = mfma32(qa[c], kf[c], s);
-          if constexpr (WANT_DK) dpv = mfma32(da[c], vf[c], dpv);
-        }
-      } else {
-        // the dK part holds K and V rows: operands stream four reads ahead instead
-        constexpr int LA = 4;
-        auto rd = [&](int j) {
-          return *(const bf16x8*)(((j & 1) ? DO : Q) + 32 * qb * C::ROWB + off.ro[j >> 1]);
-        };
-        bf16x8 opa[LA];
-#pragma unroll
-        for (int j = 0; j < LA; ++j) opa[j] = rd(j);
-#pragma unroll
-        for (int j = 0; j < 2 * C::NC; ++j) {
-          if (j & 1) dpv = mfma32(opa[j % LA], vf[j >> 1], dpv);
-          else s = mfma32(opa[j % LA], kf[j >> 1], s);
-          if (j + LA < 2 * C::NC) opa[j % LA] = rd(j + LA);
-        }
+      for (int c = 0; c < C::NC; ++c) {
+        s = mfma32(qa[c], kf[c], s);
+        dpv = mfma32(da[c], vf[c], dpv);
       }
       // rows of s / dpv: query 32qb + 8g + 4h + j, column: this lane's key
       f32x4 L4[4], D4[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         L4[g] = *(const f32x4*)(slse[cur] + 32 * qb + 8 * g + 4 * h);
-        if constexpr (WANT_DK) D4[g] = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
+        D4[g] = *(const f32x4*)(sdelta[cur] + 32 * qb + 8 * g + 4 * h);
       }
       // raw LSE: -L log2e; a row without any visible key (LSE = -inf) only occurs in
       // tiles that are not full, where the mask below replaces its weights by 0
@@ -264,8 +246,8 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
       bf16x8 pa[2], dsa[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        if constexpr (WANT_DV) pa[r >> 3][r & 7] = (__bf16)p[r];
-        if constexpr (WANT_DK) dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
+        pa[r >> 3][r & 7] = (__bf16)p[r];
+        dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
       }
       // dV += P^T dO, dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
 #pragma unroll
@@ -274,26 +256,17 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
         bf16x8 ob[C::NDB], qv[C::NDB];
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          if constexpr (WANT_DV)
-            ob[db] = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
-                          lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
-          if constexpr (WANT_DK)
-            qv[db] = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
-                          lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
+          ob[db] = cat8(lds_read_tr4((const __bf16*)(DO + rb + off.tro[0][db])),
+                        lds_read_tr4((const __bf16*)(DO + rb + off.tro[1][db])));
+          qv[db] = cat8(lds_read_tr4((const __bf16*)(Q + rb + off.tro[0][db])),
+                        lds_read_tr4((const __bf16*)(Q + rb + off.tro[1][db])));
         }
         __builtin_amdgcn_sched_barrier(0);
+        // both accumulators live in AGPRs, away from the working set
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          // with both accumulators (128 registers at D = 128) they live in AGPRs; a single
-          // one stays in VGPRs, which keeps the register split free
-          if constexpr (PART == 0) {
-            mfma32_agpr(dv[db], pa[tt], ob[db]);
-            mfma32_agpr(dk[db], dsa[tt], qv[db]);
-          } else if constexpr (WANT_DV) {
-            dv[db] = mfma32(pa[tt], ob[db], dv[db]);
-          } else {
-            dk[db] = mfma32(dsa[tt], qv[db], dk[db]);
-          }
+          mfma32_agpr(dv[db], pa[tt], ob[db]);
+          mfma32_agpr(dk[db], dsa[tt], qv[db]);
         }
       }
     }
@@ -301,12 +274,10 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 
   // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
   if (n_items <= 0 && a.acc_kv) return;
-  if constexpr (PART == 0) {
 #pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      mfma_agpr_drain(dk[db]);
-      mfma_agpr_drain(dv[db]);
-    }
+  for (int db = 0; db < C::NDB; ++db) {
+    mfma_agpr_drain(dk[db]);
+    mfma_agpr_drain(dv[db]);
   }
   // accumulate: lane holds column d = 32db + lq, rows key kw0 + 8g + 4h + j. The wave's 32
   // rows go through a buffer resource bounded at its last key, so rows past Tk read as zero
@@ -334,8 +305,240 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
             __builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * acc[db][r]), rs, offset(db, r),
             0, 0);
   };
-  if constexpr (WANT_DK) add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale);
-  if constexpr (WANT_DV) add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f);
+  add_rows(a.dk + b * a.dk_sb + kvh * a.dk_sh, a.dk_st, dk, a.scale);
+  add_rows(a.dv + b * a.dv_sb + kvh * a.dv_sh, a.dv_st, dv, 1.f);
+}
+
+// ------------------------------------------------------------------ dK / dV, paired waves
+// Eight waves, 128 keys per workgroup (one workgroup per CU); waves w and w + 4 own the
+// same 32 keys. Wave w forms S = Q K^T and the weights P, hands P (fp32) to its partner
+// through LDS and accumulates dV += P^T dO; wave w + 4 forms dP = dO V^T, takes P, forms
+// dS = P (dP - delta) and accumulates dK += dS^T Q. A pair thus forms each of the four
+// products once (8·D flops per pair of the block, S no longer formed twice), and each wave
+// holds one accumulator and one of the K / V fragments, so two waves fit per SIMD. Two
+// barriers per query tile: the tile has landed; P of the tile is in LDS. The arithmetic of
+// every product and of dS is that of dkdv_body, so the results are the same bits.
+constexpr int kPairWaves = 8;
+
+template <int D, int NS>
+struct DkdvPairLds {
+  alignas(1024) char sq[NS][BCfg<D>::TILEB];
+  alignas(1024) char sdo[NS][BCfg<D>::TILEB];
+  alignas(16) float slse[NS][kTile];
+  alignas(16) float sdelta[NS][kTile];
+  alignas(16) f32x4 sp[kNW][2][4][64];  // [pair][32-row block][16-byte quarter][lane]: P
+};
+
+template <int D, int NS>
+__device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_kt, DkdvPairLds<D, NS>& sm) {
+  using C = BCfg<D>;
+  constexpr int NIP = kTile * C::CPR / (64 * kPairWaves);  // direct loads per wave per tile (Q, dO each)
+  static_assert(NIP >= 1, "tile layout");
+  auto& sq = sm.sq;
+  auto& sdo = sm.sdo;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, h = l >> 5, lq = l & 31;
+  const bool pw = w < kNW;  // forms S, P and dV (else dP, dS and dK)
+  const int kw = w & (kNW - 1);
+  const int bh = Lg / n_kt;  // (b, KV head)
+  const int kt = Lg - bh * n_kt;
+  const int H_kv = a.H / a.G;
+  const int b = bh / H_kv, kvh = bh - b * H_kv;
+  const int kc0 = kt * kKeysPerWG;  // first key of the workgroup
+  const int kw0 = kc0 + 32 * kw;    // first key of the pair
+  const int key = kw0 + lq;         // this lane's key
+  const bool key_ok = key < a.Tk;
+
+  const int qlo = a.causal ? a.qm.count_lt(a.km.pos(key_ok ? key : a.Tk - 1)) : 0;
+  const int wave_last_key = (kw0 + 31 < a.Tk ? kw0 + 31 : a.Tk - 1);
+  const int wave_qlo = a.causal ? a.qm.count_lt(a.km.pos(wave_last_key)) : 0;
+  const int q_first = a.causal ? a.qm.count_lt(a.km.pos(kc0)) : 0;
+  const int t_begin = q_first / kTile;
+  const int t_end = (a.Tq + kTile - 1) / kTile;
+  const int n = t_end - t_begin;
+  const int n_items = n * a.G;  // (query head of the group, tile), head-major
+  const float sl2 = a.scale * kLog2e;
+
+  int ld_row[NIP], ld_col[NIP];
+  unsigned qo[NIP], oo[NIP];
+#pragma unroll
+  for (int i = 0; i < NIP; ++i) {
+    const int p = (w * NIP + i) * 64 + l;
+    ld_row[i] = p / C::CPR;
+    ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
+    qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
+    oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
+  }
+  // LSE rows of a tile come with the first four waves, delta rows with the others (16 each)
+  const int sr = 16 * kw + (l & 15);
+  const unsigned lo_row = (unsigned)(sr * (pw ? a.lse.st : a.delta.st) * 4);
+  auto issue_tile = [&](int it, int buf) {
+    const int hq = kvh * a.G + it / n;
+    const int t = t_begin + it % n;
+    const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hq * a.q.sh;
+    const __bf16* dop = (const __bf16*)a.dout.p + b * a.dout.sb + hq * a.dout.sh;
+    const float* rp = pw ? (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh
+                         : (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
+    const int64_t rst = pw ? a.lse.st : a.delta.st;
+    const int q0 = t * kTile;
+    const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
+    const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
+    const bool tail = q0 + kTile > a.Tq;  // rows past the end repeat the last row (masked)
+#pragma unroll
+    for (int i = 0; i < NIP; ++i) {
+      unsigned q_off = qo[i], o_off = oo[i];
+      if (tail) {
+        const int r = min(ld_row[i], a.Tq - 1 - q0);
+        q_off = (unsigned)((r * a.q.st + ld_col[i]) * 2);
+        o_off = (unsigned)((r * a.dout.st + ld_col[i]) * 2);
+      }
+      load_lds16(qbase, q_off, sq[buf] + (w * NIP + i) * 1024);
+      load_lds16(obase, o_off, sdo[buf] + (w * NIP + i) * 1024);
+    }
+    if (l < 16) {
+      unsigned r_off = lo_row;
+      if (tail) r_off = (unsigned)(min(sr, a.Tq - 1 - q0) * rst * 4);
+      load_lds4(rp + (int64_t)q0 * rst, r_off, pw ? &sm.slse[buf][16 * kw] : &sm.sdelta[buf][16 * kw]);
+    }
+  };
+
+  const Offs<D> off(l);
+  f32x16 acc[C::NDB];  // dV (first four waves) or dK
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_items) issue_tile(j, j);
+
+  // K row (first four waves) or V row of this lane's key: B operand, column = key
+  bf16x8 kvf[C::NC];
+  {
+    const __bf16* src = pw ? (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st
+                           : (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
+#pragma unroll
+    for (int c = 0; c < C::NC; ++c) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      kvf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(src + 16 * c + 8 * h) : z);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(kvf[c]));
+
+  for (int it = 0; it < n_items; ++it) {
+    const int t = t_begin + it % n;
+    const int cur = it % NS;
+    wait_tiles<2 * NIP + 1>(min(NS - 2, n_items - 1 - it));
+    __syncthreads();  // tile it visible; every wave is done with tile it-1 and its P
+    if (it + NS - 1 < n_items) issue_tile(it + NS - 1, (it + NS - 1) % NS);
+    const char* Q = sq[cur];
+    const char* DO = sdo[cur];
+    const int q0 = t * kTile;
+    const bool full = (q0 + kTile <= a.Tq) && (kw0 + 31 < a.Tk) && (q0 >= wave_qlo);
+
+    // ---- S (or dP) of both 32-row blocks: A operand = Q (dO) rows from LDS, B = this lane's K (V)
+    const char* A = pw ? Q : DO;
+    f32x16 sd[2];
+    bf16x8 pa[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      constexpr int LA = 4;
+      auto rd = [&](int c) { return *(const bf16x8*)(A + 32 * qb * C::ROWB + off.ro[c]); };
+      bf16x8 opa[LA];
+#pragma unroll
+      for (int c = 0; c < LA; ++c) opa[c] = rd(c);
+      f32x16 x = f32x16{};
+#pragma unroll
+      for (int c = 0; c < C::NC; ++c) {
+        x = mfma32(opa[c % LA], kvf[c], x);
+        if (c + LA < C::NC) opa[c % LA] = rd(c + LA);
+      }
+      sd[qb] = x;
+    }
+    if (pw) {
+      // P = exp(S sigma - LSE) on the visible pairs, into LDS (fp32) for the partner
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x4 L4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) L4[g] = *(const f32x4*)(sm.slse[cur] + 32 * qb + 8 * g + 4 * h);
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(sd[qb][r], sl2, L4[r >> 2][r & 3] * -kLog2e));
+        if (!full) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+            p[r] = (key_ok && qrow >= qlo && qrow < a.Tq) ? p[r] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) sm.sp[kw][qb][g][l] = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pa[qb][r >> 3][r & 7] = (__bf16)p[r];
+      }
+    }
+    __syncthreads();  // P of the tile in LDS
+
+    // ---- dV += P^T dO, or dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      bf16x8 xa[2];
+      if (pw) {
+        xa[0] = pa[qb][0];
+        xa[1] = pa[qb][1];
+      } else {
+        f32x4 D4[4], P4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          D4[g] = *(const f32x4*)(sm.sdelta[cur] + 32 * qb + 8 * g + 4 * h);
+          P4[g] = sm.sp[kw][qb][g][l];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          xa[r >> 3][r & 7] = (__bf16)(P4[r >> 2][r & 3] * (sd[qb][r] - D4[r >> 2][r & 3]));
+      }
+      const char* Bsrc = pw ? DO : Q;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int rb = (32 * qb + 16 * tt) * C::ROWB;
+        bf16x8 ob[C::NDB];
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          ob[db] = cat8(lds_read_tr4((const __bf16*)(Bsrc + rb + off.tro[0][db])),
+                        lds_read_tr4((const __bf16*)(Bsrc + rb + off.tro[1][db])));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(xa[tt], ob[db], acc[db]);
+      }
+    }
+  }
+
+  // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
+  if (n_items <= 0 && a.acc_kv) return;
+  const int rows = min(32, a.Tk - kw0);
+  float* base = pw ? a.dv + b * a.dv_sb + kvh * a.dv_sh : a.dk + b * a.dk_sb + kvh * a.dk_sh;
+  const int64_t st = pw ? a.dv_st : a.dk_st;
+  const float mul = pw ? 1.f : a.scale;
+  const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
+  const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
+  const auto rl = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, a.acc_kv ? bytes : 0,
+                                                    kBufferFlags);
+  auto offset = [&](int db, int r) { return (int)(((8 * (r >> 2) + 4 * h + (r & 3)) * st + lq) * 4) + 128 * db; };
+  unsigned old[C::NDB][16];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) old[db][r] = __builtin_amdgcn_raw_buffer_load_b32(rl, offset(db, r), 0, 0);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      __builtin_amdgcn_raw_buffer_store_b32(
+          __builtin_bit_cast(unsigned, __builtin_bit_cast(float, old[db][r]) + mul * acc[db][r]), rs, offset(db, r), 0,
+          0);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -632,10 +835,16 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   }
 }
 
-template <int D, int NS, int PART>
-__global__ __launch_bounds__(256, PART == 0 ? 1 : 2) void dkdv_kernel(BwdArgs a, int n_kt) {
+template <int D, int NS>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   __shared__ DkdvLds<D, NS> sm;
-  dkdv_body<D, NS, PART>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+  dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+}
+
+template <int D, int NS>
+__global__ __launch_bounds__(64 * kPairWaves, 1) void dkdv_pair_kernel(BwdArgs a, int n_kt) {
+  __shared__ DkdvPairLds<D, NS> sm;
+  dkdv_pair_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
 template <int D, int NS, int KS>
@@ -661,7 +870,7 @@ __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, 
   const int id = blockIdx.x;
   if (id < n_kv_pad) {
     const int L = xcd_remap(id, n_kv_pad);
-    if (L < n_kv) dkdv_body<D, NSK, 0>(a, L, n_kt, sm.kv);
+    if (L < n_kv) dkdv_body<D, NSK>(a, L, n_kt, sm.kv);
   } else {
     dq_body<D, NSQ, KSQ>(a, xcd_remap(id - n_kv_pad, gridDim.x - n_kv_pad), n_qt, sm.q);
   }
@@ -694,22 +903,11 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
     }
   }
   if (which & 1) {
-    // At D = 128 both accumulators together allow one wave per SIMD. With at
-    // least four workgroups per CU the half runs instead as two launches (dV,
-    // then dK) that each hold one accumulator and keep two waves per SIMD; S is
-    // then formed twice more. Smaller grids (grouped heads) keep one launch:
-    // two resident workgroups per CU would leave the heaviest ones as a tail.
-    bool two = false;
-    if constexpr (D == 128) {
-      two = bkv * n_kt >= 1024;
-      if (two) {
-        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 1>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((dkdv_kernel<D, NSK, 2>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
-      }
-    }
-    if (!two) hipLaunchKernelGGL((dkdv_kernel<D, NSK, 0>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
+    if constexpr (D == 128)
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0, s, a,
+                         n_kt);
+    else
+      hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -580,15 +580,15 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
     assert acc[0].abs().sum() > 0
 
 
-def test_dkdv_two_launch_form_matches_one_launch_and_oracle():
-    # At D = 128 a dK/dV grid of at least 1024 workgroups runs as a dV launch and a dK launch;
-    # smaller grids run one launch holding both accumulators. Both forms take every MFMA chain
-    # in the same order, so 16 heads at once (1024 workgroups of 128 keys) must equal the same
-    # heads two at a time (128 workgroups) bit for bit. Sampled keys are checked against the
-    # oracle: the last keys (every query that sees them is among the last rows) and key 0 of
-    # one head over all 8192 rows.
+def test_dkdv_paired_waves_grid_independent_and_oracle():
+    # At D = 128 a dK/dV workgroup is eight waves: two waves share 32 keys, one forming P and
+    # dV, the other dP, dS and dK with P taken from LDS. A key's arithmetic does not depend on
+    # the grid, so 16 heads at once (1024 workgroups of 128 keys, four per CU in turn) must
+    # equal the same heads two at a time (128 workgroups) bit for bit. Sampled keys are
+    # checked against the oracle: the last keys (every query that sees them is among the last
+    # rows) and key 0 of one head over all 8192 rows.
     B, H, T, D = 1, 16, 8192, 128
-    log(f"dkdv two-launch form B{B} H{H} T{T} D{D}")
+    log(f"dkdv paired waves B{B} H{H} T{T} D{D}")
     q, k, v, do = draw_shape(B, H, T, D, torch.bfloat16, seed=131, n=4)
     m = (T, T, 0, 0)
     qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
