@@ -14,8 +14,9 @@
 //     and dS^T then feed the A operand of dV += P^T dO and dK += dS^T Q
 //     straight from registers, and dO / Q enter as B operands through the
 //     transposing LDS read. At D = 64 each of 4 waves owns 32 keys with both
-//     accumulators; at D = 128 two waves share 32 keys, one forming P and dV,
-//     the other dP, dS and dK (8 waves, P handed over through LDS).
+//     accumulators; at D = 128 two waves share 32 keys, each forming P and dS
+//     for half of a tile's rows, one accumulating dV and the other dK over the
+//     whole tile (8 waves, the halves exchanged through LDS).
 //   * dq: a workgroup owns 128 query rows and walks the visible key tiles, like
 //     the forward: S^T = K Q^T and dP^T = V dO^T give one query per lane, and
 //     dQ^T += K^T dS^T reads K^T with the transposing LDS read.
@@ -311,13 +312,15 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 
 // ------------------------------------------------------------------ dK / dV, paired waves
 // Eight waves, 128 keys per workgroup (one workgroup per CU); waves w and w + 4 own the
-// same 32 keys. Wave w forms S = Q K^T and the weights P, hands P (fp32) to its partner
-// through LDS and accumulates dV += P^T dO; wave w + 4 forms dP = dO V^T, takes P, forms
-// dS = P (dP - delta) and accumulates dK += dS^T Q. A pair thus forms each of the four
-// products once (8·D flops per pair of the block, S no longer formed twice), and each wave
-// holds one accumulator and one of the K / V fragments, so two waves fit per SIMD. Two
-// barriers per query tile: the tile has landed; P of the tile is in LDS. The arithmetic of
-// every product and of dS is that of dkdv_body, so the results are the same bits.
+// same 32 keys and hold both their K and V rows. Of each 64-row query tile, wave w takes
+// rows 0-31 and wave w + 4 rows 32-63: each forms S and dP of its rows, then P and
+// dS = P (dP - delta) in bf16. Wave w keeps P and hands dS to its partner through LDS,
+// wave w + 4 keeps dS and hands P over; after a barrier wave w accumulates
+// dV += P^T dO and wave w + 4 dK += dS^T Q over all 64 rows. Each pair forms each of the
+// four products once (8·D flops per pair of the block), both waves do the same work, and
+// each holds one accumulator, so two waves fit per SIMD. Two barriers per query tile: the
+// tile has landed; the exchanged halves are in LDS. The arithmetic of every product and
+// of dS is that of dkdv_body, so the results are the same bits.
 constexpr int kPairWaves = 8;
 
 template <int D, int NS>
@@ -326,7 +329,7 @@ struct DkdvPairLds {
   alignas(1024) char sdo[NS][BCfg<D>::TILEB];
   alignas(16) float slse[NS][kTile];
   alignas(16) float sdelta[NS][kTile];
-  alignas(16) f32x4 sp[kNW][2][4][64];  // [pair][32-row block][16-byte quarter][lane]: P
+  alignas(16) bf16x8 sx[kNW][2][2][64];  // [pair][from wave w / w + 4][8-value half][lane]
 };
 
 template <int D, int NS>
@@ -340,7 +343,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const bool pw = w < kNW;  // forms S, P and dV (else dP, dS and dK)
+  const int hb = w >= kNW ? 1 : 0;  // 32-row block of each tile this wave forms; 0: keeps dV
   const int kw = w & (kNW - 1);
   const int bh = Lg / n_kt;  // (b, KV head)
   const int kt = Lg - bh * n_kt;
@@ -372,16 +375,17 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
     oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
   }
   // LSE rows of a tile come with the first four waves, delta rows with the others (16 each)
+  const bool lse_loader = hb == 0;
   const int sr = 16 * kw + (l & 15);
-  const unsigned lo_row = (unsigned)(sr * (pw ? a.lse.st : a.delta.st) * 4);
+  const unsigned lo_row = (unsigned)(sr * (lse_loader ? a.lse.st : a.delta.st) * 4);
   auto issue_tile = [&](int it, int buf) {
     const int hq = kvh * a.G + it / n;
     const int t = t_begin + it % n;
     const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hq * a.q.sh;
     const __bf16* dop = (const __bf16*)a.dout.p + b * a.dout.sb + hq * a.dout.sh;
-    const float* rp = pw ? (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh
-                         : (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
-    const int64_t rst = pw ? a.lse.st : a.delta.st;
+    const float* rp = lse_loader ? (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh
+                                 : (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
+    const int64_t rst = lse_loader ? a.lse.st : a.delta.st;
     const int q0 = t * kTile;
     const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
     const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
@@ -400,12 +404,12 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
     if (l < 16) {
       unsigned r_off = lo_row;
       if (tail) r_off = (unsigned)(min(sr, a.Tq - 1 - q0) * rst * 4);
-      load_lds4(rp + (int64_t)q0 * rst, r_off, pw ? &sm.slse[buf][16 * kw] : &sm.sdelta[buf][16 * kw]);
+      load_lds4(rp + (int64_t)q0 * rst, r_off, lse_loader ? &sm.slse[buf][16 * kw] : &sm.sdelta[buf][16 * kw]);
     }
   };
 
   const Offs<D> off(l);
-  f32x16 acc[C::NDB];  // dV (first four waves) or dK
+  f32x16 acc[C::NDB];  // dV (waves 0-3) or dK (waves 4-7)
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
 
@@ -413,94 +417,89 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
   for (int j = 0; j < NS - 1; ++j)
     if (j < n_items) issue_tile(j, j);
 
-  // K row (first four waves) or V row of this lane's key: B operand, column = key
-  bf16x8 kvf[C::NC];
+  // K and V rows of this lane's key (B operands: column = key, 8 consecutive d)
+  bf16x8 kf[C::NC], vf[C::NC];
   {
-    const __bf16* src = pw ? (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st
-                           : (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
+    const __bf16* kk = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh + (int64_t)key * a.k.st;
+    const __bf16* vv = (const __bf16*)a.v.p + b * a.v.sb + kvh * a.v.sh + (int64_t)key * a.v.st;
 #pragma unroll
     for (int c = 0; c < C::NC; ++c) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      kvf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(src + 16 * c + 8 * h) : z);
+      kf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(kk + 16 * c + 8 * h) : z);
+      vf[c] = __builtin_bit_cast(bf16x8, key_ok ? ldg16(vv + 16 * c + 8 * h) : z);
     }
   }
 #pragma unroll
-  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(kvf[c]));
+  for (int c = 0; c < C::NC; ++c) asm volatile("" ::"v"(kf[c]), "v"(vf[c]));
 
   for (int it = 0; it < n_items; ++it) {
     const int t = t_begin + it % n;
     const int cur = it % NS;
     wait_tiles<2 * NIP + 1>(min(NS - 2, n_items - 1 - it));
-    __syncthreads();  // tile it visible; every wave is done with tile it-1 and its P
+    __syncthreads();  // tile it visible; every wave is done with tile it-1 and the exchange
     if (it + NS - 1 < n_items) issue_tile(it + NS - 1, (it + NS - 1) % NS);
     const char* Q = sq[cur];
     const char* DO = sdo[cur];
     const int q0 = t * kTile;
     const bool full = (q0 + kTile <= a.Tq) && (kw0 + 31 < a.Tk) && (q0 >= wave_qlo);
 
-    // ---- S (or dP) of both 32-row blocks: A operand = Q (dO) rows from LDS, B = this lane's K (V)
-    const char* A = pw ? Q : DO;
-    f32x16 sd[2];
-    bf16x8 pa[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    // ---- S = Q K^T and dP = dO V^T of this wave's 32 rows (operands streamed from LDS)
+    f32x16 s = f32x16{}, dpv = f32x16{};
+    {
       constexpr int LA = 4;
-      auto rd = [&](int c) { return *(const bf16x8*)(A + 32 * qb * C::ROWB + off.ro[c]); };
+      auto rd = [&](int j) {
+        return *(const bf16x8*)(((j & 1) ? DO : Q) + 32 * hb * C::ROWB + off.ro[j >> 1]);
+      };
       bf16x8 opa[LA];
 #pragma unroll
-      for (int c = 0; c < LA; ++c) opa[c] = rd(c);
-      f32x16 x = f32x16{};
+      for (int j = 0; j < LA; ++j) opa[j] = rd(j);
 #pragma unroll
-      for (int c = 0; c < C::NC; ++c) {
-        x = mfma32(opa[c % LA], kvf[c], x);
-        if (c + LA < C::NC) opa[c % LA] = rd(c + LA);
-      }
-      sd[qb] = x;
-    }
-    if (pw) {
-      // P = exp(S sigma - LSE) on the visible pairs, into LDS (fp32) for the partner
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x4 L4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) L4[g] = *(const f32x4*)(sm.slse[cur] + 32 * qb + 8 * g + 4 * h);
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(sd[qb][r], sl2, L4[r >> 2][r & 3] * -kLog2e));
-        if (!full) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qrow = q0 + 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-            p[r] = (key_ok && qrow >= qlo && qrow < a.Tq) ? p[r] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) sm.sp[kw][qb][g][l] = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pa[qb][r >> 3][r & 7] = (__bf16)p[r];
+      for (int j = 0; j < 2 * C::NC; ++j) {
+        if (j & 1) dpv = mfma32(opa[j % LA], vf[j >> 1], dpv);
+        else s = mfma32(opa[j % LA], kf[j >> 1], s);
+        if (j + LA < 2 * C::NC) opa[j % LA] = rd(j + LA);
       }
     }
-    __syncthreads();  // P of the tile in LDS
+    // rows of s / dpv: query 32hb + 8g + 4h + j, column: this lane's key
+    f32x4 L4[4], D4[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      L4[g] = *(const f32x4*)(sm.slse[cur] + 32 * hb + 8 * g + 4 * h);
+      D4[g] = *(const f32x4*)(sm.sdelta[cur] + 32 * hb + 8 * g + 4 * h);
+    }
+    float p[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], sl2, L4[r >> 2][r & 3] * -kLog2e));
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qrow = q0 + 32 * hb + 8 * (r >> 2) + 4 * h + (r & 3);
+        p[r] = (key_ok && qrow >= qlo && qrow < a.Tq) ? p[r] : 0.f;
+      }
+    }
+    bf16x8 pa[2], dsa[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      pa[r >> 3][r & 7] = (__bf16)p[r];
+      dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
+    }
+    // keep what this wave accumulates (P for dV, dS for dK); hand the other to the partner
+    bf16x8 mine[2][2];  // [32-row block][8-value half]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bf16x8 keep = hb == 0 ? pa[i] : dsa[i];
+      const bf16x8 give = hb == 0 ? dsa[i] : pa[i];
+      mine[hb][i] = keep;
+      sm.sx[kw][hb][i][l] = give;
+    }
+    __syncthreads();  // the partner's half of the tile in LDS
+#pragma unroll
+    for (int i = 0; i < 2; ++i) mine[1 - hb][i] = sm.sx[kw][1 - hb][i][l];
 
     // ---- dV += P^T dO, or dK += dS^T Q ; B operand rows = queries 32qb + 16tt + 4h + {0..3}, +8
+    const char* Bsrc = hb == 0 ? DO : Q;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      bf16x8 xa[2];
-      if (pw) {
-        xa[0] = pa[qb][0];
-        xa[1] = pa[qb][1];
-      } else {
-        f32x4 D4[4], P4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          D4[g] = *(const f32x4*)(sm.sdelta[cur] + 32 * qb + 8 * g + 4 * h);
-          P4[g] = sm.sp[kw][qb][g][l];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          xa[r >> 3][r & 7] = (__bf16)(P4[r >> 2][r & 3] * (sd[qb][r] - D4[r >> 2][r & 3]));
-      }
-      const char* Bsrc = pw ? DO : Q;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int rb = (32 * qb + 16 * tt) * C::ROWB;
@@ -511,17 +510,18 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
                         lds_read_tr4((const __bf16*)(Bsrc + rb + off.tro[1][db])));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(xa[tt], ob[db], acc[db]);
+        for (int db = 0; db < C::NDB; ++db) acc[db] = mfma32(mine[qb][tt], ob[db], acc[db]);
       }
     }
   }
 
   // no query of this block sees these keys: nothing to add (an overwrite still writes zeros)
   if (n_items <= 0 && a.acc_kv) return;
+  const bool dv_wave = hb == 0;
   const int rows = min(32, a.Tk - kw0);
-  float* base = pw ? a.dv + b * a.dv_sb + kvh * a.dv_sh : a.dk + b * a.dk_sb + kvh * a.dk_sh;
-  const int64_t st = pw ? a.dv_st : a.dk_st;
-  const float mul = pw ? 1.f : a.scale;
+  float* base = dv_wave ? a.dv + b * a.dv_sb + kvh * a.dv_sh : a.dk + b * a.dk_sb + kvh * a.dk_sh;
+  const int64_t st = dv_wave ? a.dv_st : a.dk_st;
+  const float mul = dv_wave ? 1.f : a.scale;
   const int bytes = rows > 0 ? ((rows - 1) * (int)st + D) * 4 : 0;  // rows never overlap: st >= D
   const auto rs = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, bytes, kBufferFlags);
   const auto rl = __builtin_amdgcn_make_buffer_rsrc(base + (int64_t)kw0 * st, (short)0, a.acc_kv ? bytes : 0,

@@ -581,8 +581,9 @@ def test_split_backward_and_step_driven_forward_match_bitwise():
 
 
 def test_dkdv_paired_waves_grid_independent_and_oracle():
-    # At D = 128 a dK/dV workgroup is eight waves: two waves share 32 keys, one forming P and
-    # dV, the other dP, dS and dK with P taken from LDS. A key's arithmetic does not depend on
+    # At D = 128 a dK/dV workgroup is eight waves: two waves share 32 keys, each forming P and
+    # dS for half of a tile's rows and handing one of them to the other through LDS; one
+    # accumulates dV, the other dK. A key's arithmetic does not depend on
     # the grid, so 16 heads at once (1024 workgroups of 128 keys, four per CU in turn) must
     # equal the same heads two at a time (128 workgroups) bit for bit. Sampled keys are
     # checked against the oracle: the last keys (every query that sees them is among the last
