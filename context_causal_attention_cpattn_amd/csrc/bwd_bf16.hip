@@ -23,6 +23,7 @@
 // Tiles are staged through LDS with direct global->LDS loads into the
 // swizzled, unpadded layout of common.h (double buffered, one barrier per tile).
 
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -848,9 +849,13 @@ __global__ __launch_bounds__(64 * kPairWaves, 1) void dkdv_pair_kernel(BwdArgs a
 }
 
 template <int D, int NS, int KS>
-__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt) {
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdArgs a, int n_qt, int vary) {
   __shared__ DqLds<D, NS, KS> sm;
-  dq_body<D, NS, KS>(a, xcd_remap(blockIdx.x, gridDim.x), n_qt, sm);
+  // query tiles heavy first; with `vary` (the tiles' work differs) the heavy tiles of all
+  // the heads an XCD holds first
+  int head, rank;
+  xcd_tile(blockIdx.x, gridDim.x, n_qt, vary != 0, head, rank);
+  dq_body<D, NS, KS>(a, head * n_qt + rank, n_qt, sm);
 }
 
 // Both halves of the block backward in one grid: the first n_kv workgroups
@@ -914,11 +919,14 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   if (which & 2) {
     if constexpr (D == 64) {
       if (split) {
-        hipLaunchKernelGGL((dq_kernel<D, NSQ, 2>), dim3((unsigned)(bh * n_qt2)), dim3(64 * kNW), 0, s, a, n_qt2);
+        hipLaunchKernelGGL((dq_kernel<D, NSQ, 2>), dim3((unsigned)(bh * n_qt2)), dim3(64 * kNW), 0, s, a, n_qt2, 0);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((dq_kernel<D, NSQ, 1>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt);
+    // at D = 128, a causal block whose first and last row tiles see different numbers of keys
+    const int vary = D == 128 && a.causal &&
+                     a.km.count_le(a.qm.pos(std::min(kQPerWG, a.Tq) - 1)) != a.km.count_le(a.qm.pos(a.Tq - 1));
+    hipLaunchKernelGGL((dq_kernel<D, NSQ, 1>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt, vary);
     return hipGetLastError();
   }
   return hipSuccess;

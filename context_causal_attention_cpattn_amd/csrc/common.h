@@ -154,4 +154,25 @@ __device__ __forceinline__ int xcd_remap(int wg, int n) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Workgroup id -> (head, rank) for a grid of heads x n_t tiles each, rank 0 the
+// heaviest tile of its head. The tiles of a head run on one XCD, as with
+// xcd_remap. When `vary` (the tiles of a head differ in work) and an XCD's share
+// of the grid is whole heads, its workgroups take the heaviest tiles of all of
+// its heads first (head-minor order), so that no head's heavy tiles are dispatched
+// last; otherwise head by head (head-major), keeping one head's tiles together.
+__device__ __forceinline__ void xcd_tile(int wg, int n, int n_t, bool vary, int& head, int& rank) {
+  const int per = n >> 3, rem = n & 7;
+  const int x = wg & 7, slot = wg >> 3;
+  const int L0 = x * per + (x < rem ? x : rem), cnt = per + (x < rem ? 1 : 0);
+  if (vary && L0 % n_t == 0 && cnt % n_t == 0 && cnt > n_t) {
+    const int nh = cnt / n_t;
+    head = L0 / n_t + slot % nh;
+    rank = slot / nh;
+  } else {
+    const int L = L0 + slot;
+    head = L / n_t;
+    rank = L - head * n_t;
+  }
+}
+
 }  // namespace cpattn

@@ -32,11 +32,13 @@
 //     score exceeds it by more than 2^8, so the accumulator is rarely rescaled
 //     (exact: O and the row sum always share the same reference max);
 //   * workgroup ids are remapped so that the query tiles of one (b, h) run on
-//     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first;
+//     one XCD and share its K/V in that XCD's L2; heavy (late) tiles go first,
+//     on a causal block at D = 128 those of all the heads an XCD holds;
 //   * the loop is software pipelined so that each wave keeps its matrix cores
 //     and its vector ALUs busy at the same time (see fwd_bf16_kernel).
 // The variant with fused rotary embedding lives in fwd_rope_bf16.hip.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -94,7 +96,7 @@ __device__ __forceinline__ void wait_units(int units) {
 // NW is the number of waves of a workgroup (4: two workgroups per CU, 8: one).
 // With SPLIT_LOAD only the upper half of a key share's waves issue its tile loads.
 template <int D, int NS, int KS, int NW, bool SPLIT_LOAD>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, int n_qt) {
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, int n_qt, int vary) {
   using C = Cfg<D>;
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
   static_assert(KS == 1 || (KS == 2 && D == 64), "key split: 64-wide heads only");
@@ -109,9 +111,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
   const int rb = w % NR;  // row block of this wave
   const int kh = w / NR;  // key share of this wave: tiles kh, kh + KS, kh + 2 KS, ...
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / n_qt;
-  const int qt = n_qt - 1 - (L - bh * n_qt);
+  // (head, query tile), heavy tiles first; with `vary` (the tiles' work differs) the heavy
+  // tiles of all the heads an XCD holds first
+  int bh, rank;
+  xcd_tile(blockIdx.x, gridDim.x, n_qt, vary != 0, bh, rank);
+  const int qt = n_qt - 1 - rank;
   const int b = bh / a.H, hh = bh - b * a.H;
   const int q0 = a.row_begin + qt * ROWS;
   const int row = q0 + 32 * rb + lq;
@@ -498,8 +502,11 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if constexpr (D == 128) {
     constexpr int NW = 8;
     const int n_qt = (rows + 32 * NW - 1) / (32 * NW);
+    // a causal block whose first and last row tiles see different numbers of keys
+    const int first_last = std::min(a.row_begin + 32 * NW, a.row_end) - 1;
+    const int vary = a.causal && a.km.count_le(a.qm.pos(first_last)) != a.km.count_le(a.qm.pos(a.row_end - 1));
     hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1, NW, true>), dim3((unsigned)(n_qt * bh)), dim3(64 * NW), 0, s, a,
-                       n_qt);
+                       n_qt, vary);
     return hipGetLastError();
   } else {
     const int64_t grid1 = (int64_t)((rows + kBM - 1) / kBM) * bh;
@@ -507,11 +514,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     if (grid1 < 512) {
       const int n_qt = (rows + kBM / 2 - 1) / (kBM / 2);
       hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2, kNW, false>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s,
-                         a, n_qt);
+                         a, n_qt, 0);
       return hipGetLastError();
     }
     const int n_qt = (rows + kBM - 1) / kBM;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1, kNW, false>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1, kNW, false>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt,
+                       0);
     return hipGetLastError();
   }
 }
