@@ -320,8 +320,9 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 // dV += P^T dO and wave w + 4 dK += dS^T Q over all 64 rows. Each pair forms each of the
 // four products once (8·D flops per pair of the block), both waves do the same work, and
 // each holds one accumulator, so two waves fit per SIMD. Two barriers per query tile: the
-// tile has landed; the exchanged halves are in LDS. The arithmetic of every product and
-// of dS is that of dkdv_body, so the results are the same bits.
+// tile has landed; the exchanged halves are in LDS. Only waves 0-3 issue the tile loads.
+// The arithmetic of every product and of dS is that of dkdv_body, so the results are the
+// same bits.
 constexpr int kPairWaves = 8;
 
 template <int D, int NS>
@@ -336,7 +337,7 @@ struct DkdvPairLds {
 template <int D, int NS>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_kt, DkdvPairLds<D, NS>& sm) {
   using C = BCfg<D>;
-  constexpr int NIP = kTile * C::CPR / (64 * kPairWaves);  // direct loads per wave per tile (Q, dO each)
+  constexpr int NIP = kTile * C::CPR / (64 * kNW);  // direct loads per loader wave per tile (Q, dO each)
   static_assert(NIP >= 1, "tile layout");
   auto& sq = sm.sq;
   auto& sdo = sm.sdo;
@@ -369,24 +370,23 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
   unsigned qo[NIP], oo[NIP];
 #pragma unroll
   for (int i = 0; i < NIP; ++i) {
-    const int p = (w * NIP + i) * 64 + l;
+    const int p = (kw * NIP + i) * 64 + l;
     ld_row[i] = p / C::CPR;
     ld_col[i] = ((p % C::CPR) ^ swz_mask<D>(p / C::CPR)) * 8;
     qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
     oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
   }
-  // LSE rows of a tile come with the first four waves, delta rows with the others (16 each)
-  const bool lse_loader = hb == 0;
+  // Only the dV waves (0-3) load the tiles: the dK waves go straight from the barrier to
+  // their products while the loads queue (a loader brings 16 rows of Q, dO, LSE and delta)
   const int sr = 16 * kw + (l & 15);
-  const unsigned lo_row = (unsigned)(sr * (lse_loader ? a.lse.st : a.delta.st) * 4);
   auto issue_tile = [&](int it, int buf) {
+    if (hb != 0) return;
     const int hq = kvh * a.G + it / n;
     const int t = t_begin + it % n;
     const __bf16* qp = (const __bf16*)a.q.p + b * a.q.sb + hq * a.q.sh;
     const __bf16* dop = (const __bf16*)a.dout.p + b * a.dout.sb + hq * a.dout.sh;
-    const float* rp = lse_loader ? (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh
-                                 : (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
-    const int64_t rst = lse_loader ? a.lse.st : a.delta.st;
+    const float* lp = (const float*)a.lse.p + b * a.lse.sb + hq * a.lse.sh;
+    const float* dp = (const float*)a.delta.p + b * a.delta.sb + hq * a.delta.sh;
     const int q0 = t * kTile;
     const char* qbase = (const char*)(qp + (int64_t)q0 * a.q.st);
     const char* obase = (const char*)(dop + (int64_t)q0 * a.dout.st);
@@ -399,13 +399,13 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
         q_off = (unsigned)((r * a.q.st + ld_col[i]) * 2);
         o_off = (unsigned)((r * a.dout.st + ld_col[i]) * 2);
       }
-      load_lds16(qbase, q_off, sq[buf] + (w * NIP + i) * 1024);
-      load_lds16(obase, o_off, sdo[buf] + (w * NIP + i) * 1024);
+      load_lds16(qbase, q_off, sq[buf] + (kw * NIP + i) * 1024);
+      load_lds16(obase, o_off, sdo[buf] + (kw * NIP + i) * 1024);
     }
     if (l < 16) {
-      unsigned r_off = lo_row;
-      if (tail) r_off = (unsigned)(min(sr, a.Tq - 1 - q0) * rst * 4);
-      load_lds4(rp + (int64_t)q0 * rst, r_off, lse_loader ? &sm.slse[buf][16 * kw] : &sm.sdelta[buf][16 * kw]);
+      const int r = tail ? min(sr, a.Tq - 1 - q0) : sr;
+      load_lds4(lp + (int64_t)q0 * a.lse.st, (unsigned)(r * a.lse.st * 4), &sm.slse[buf][16 * kw]);
+      load_lds4(dp + (int64_t)q0 * a.delta.st, (unsigned)(r * a.delta.st * 4), &sm.sdelta[buf][16 * kw]);
     }
   };
 
@@ -436,7 +436,7 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
   for (int it = 0; it < n_items; ++it) {
     const int t = t_begin + it % n;
     const int cur = it % NS;
-    wait_tiles<2 * NIP + 1>(min(NS - 2, n_items - 1 - it));
+    wait_tiles<2 * NIP + 2>(min(NS - 2, n_items - 1 - it));
     __syncthreads();  // tile it visible; every wave is done with tile it-1 and the exchange
     if (it + NS - 1 < n_items) issue_tile(it + NS - 1, (it + NS - 1) % NS);
     const char* Q = sq[cur];
