@@ -883,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void bwd_fused_kernel(BwdArgs a, int n_kt, 
 
 template <int D>
 hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
-  constexpr int NSK = D == 64 ? 4 : 2;  // dK/dV: stages of 64 query rows
+  constexpr int NSK = D == 64 ? 4 : 3;  // dK/dV: stages of 64 query rows
   constexpr int NSQ = 4;                // dQ: stages of 32 keys
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
