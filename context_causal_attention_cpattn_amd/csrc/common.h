@@ -32,6 +32,13 @@ struct PosMap {
   __device__ __host__ __forceinline__ int count_le(int P) const { return count_lt(P + 1); }
 };
 
+// Rotation of the pair (x1, x2) by the angle with cosine c and sine s, in one fixed
+// rounding order (the second product rounded, then one fused multiply-add), so that every
+// kernel that rotates rows -- once into a buffer or per tile inside the forward -- gives
+// the same bits: (x1 c - x2 s, x2 c + x1 s).
+__device__ __forceinline__ float rot_lo(float x1, float x2, float c, float s) { return fmaf(x1, c, -(x2 * s)); }
+__device__ __forceinline__ float rot_hi(float x1, float x2, float c, float s) { return fmaf(x2, c, x1 * s); }
+
 // One v_mfma_f32_32x32x16_bf16: C[32x32] += A[32x16] B[16x32].
 // Lane l supplies A row (l % 32), B column (l % 32), 8 consecutive k values
 // each; the accumulator holds column (l % 32), rows 8*(r/4) + 4*(l/32) + r%4.

@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
           const int i = 16 * c + 8 * h + e;
           const float cs = tb[2 * i], sn = tb[2 * i + 1];
           const float x1 = (float)qf[c][e], x2 = (float)qf[c + C::NC / 2][e];
-          qf[c][e] = (__bf16)(x1 * cs - x2 * sn);
-          qf[c + C::NC / 2][e] = (__bf16)(x2 * cs + x1 * sn);
+          qf[c][e] = (__bf16)rot_lo(x1, x2, cs, sn);
+          qf[c + C::NC / 2][e] = (__bf16)rot_hi(x1, x2, cs, sn);
         }
       }
     }
@@ -168,8 +168,8 @@ __global__ __launch_bounds__(256, 2) void fwd_rope_kernel(FwdArgs a, int n_qt) {
         for (int e = 0; e < 8; ++e) {
           const float cs = tr[4 * i + e / 2][2 * (e % 2)], sn = tr[4 * i + e / 2][2 * (e % 2) + 1];
           const float f1 = (float)x1[e], f2 = (float)x2[e];
-          y1[e] = (__bf16)(f1 * cs - f2 * sn);
-          y2[e] = (__bf16)(f2 * cs + f1 * sn);
+          y1[e] = (__bf16)rot_lo(f1, f2, cs, sn);
+          y2[e] = (__bf16)rot_hi(f1, f2, cs, sn);
         }
         const int m = C::mask(r);
         *(bf16x8*)(ks + r * C::ROWB + ((cp ^ m) * 16)) = y1;
