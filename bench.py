@@ -53,6 +53,10 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E (published)
 # after their inputs were generated on the host; with 1 warm-up and 3 timed steps the
 # per-kernel figures read up to 8 % low
 EXTRA_STEPS, EXTRA_WARMUP = 20, 20
+# Warm-up lasts at least this long (seconds of GPU time) whatever --warmup asks for: from idle,
+# the GPU clock takes a few hundred milliseconds of full load to settle, and a timing taken
+# before that reads several percent low (5 % on the 32k-window forward after 5 replays).
+WARM_S = 0.3
 HEADLINE = "win32k"
 
 
@@ -374,9 +378,11 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
     waits for the host between launches.
 
     The ``warmup`` untimed steps run the timed path: with a graph, a few eager steps, the
-    capture, then ``warmup`` replays. Eager steps leave host gaps between launches at small
-    shapes, and after them the clock had not settled: the first timing in a process read 3 %
-    below the ones after it."""
+    capture, then at least ``warmup`` replays and at least WARM_S seconds of them. Eager steps
+    leave host gaps between launches at small shapes, and after them the clock had not
+    settled. The evented steps are queued behind a spin kernel and as many graph replays as
+    the warm-up took, so that they too run at the settled clock. Returns the wall time per
+    step, the event summary, whether a graph was used and the warm-up replays run."""
     import torch
     share.build_plan(do_bwd)
     n_eager = min(warmup, 10) if graph else warmup
@@ -404,8 +410,12 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
             print(f"[bench] graph capture not used: {e}", file=sys.stderr)
             g = None
         share.build_plan(do_bwd)
-    for _ in range(warmup if g is not None else warmup - n_eager):  # eager if capture failed
-        g.replay() if g is not None else share.step()
+    n_warm, t_w = 0, time.perf_counter()
+    while n_warm < (warmup if g is not None else warmup - n_eager) or time.perf_counter() - t_w < WARM_S:
+        g.replay() if g is not None else share.step()  # eager if capture failed
+        n_warm += 1
+        if n_warm % 4 == 0:
+            torch.cuda.synchronize()  # the elapsed time is the GPU's, not the host's queueing
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -420,10 +430,13 @@ def time_steps(share, steps, warmup, do_bwd=True, graph=True):
         torch.cuda._sleep(200_000_000)  # keep the GPU busy while the host queues the evented steps
     except Exception:
         pass
+    if g is not None:
+        for _ in range(n_warm):  # the clock settles again after the spin
+            g.replay()
     for _ in range(steps):
         share.step(ev=ev)
     torch.cuda.synchronize()
-    return wall, ev.summary(), g is not None
+    return wall, ev.summary(), g is not None, n_warm
 
 
 class MergeProbe:
@@ -751,7 +764,7 @@ def main():
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
     share.fused_merge = not args.separate_merge
-    wall, kern, graphed = time_steps(share, args.steps, args.warmup, do_bwd=do_bwd, graph=not args.no_graph)
+    wall, kern, graphed, n_warm = time_steps(share, args.steps, args.warmup, do_bwd=do_bwd, graph=not args.no_graph)
     flops = share.flops(do_bwd)
     value = flops / wall / 1e12
     fam = EventLog().families(kern)
@@ -765,6 +778,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_replays": n_warm,
         "ms_per_step": round(wall * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -794,7 +808,7 @@ def main():
                 continue
             sx = Share(wx, seed_do=wx.seed + 1000)
             sx.split_bwd = wx.D == 128  # at D = 128 the two halves are separate launches anyway
-            wl, kx, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=bwd)
+            wl, kx, _, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=bwd)
             fl = sx.flops(bwd)
             key = name + ("_fwd_bwd" if name == w.name else "")
             extra[key] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
@@ -808,7 +822,7 @@ def main():
         wx = BY_NAME["win16k"]
         sx = Share(wx, seed_do=wx.seed + 1000)
         sx.fused_merge = False
-        wl, kx, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=False)
+        wl, kx, _, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=False)
         fl = sx.flops(False)
         extra["win16k_fwd_two_launch_merge"] = {
             "ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
