@@ -153,6 +153,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
   const int wave_first = q0 + 32 * rb < a.row_end ? q0 + 32 * rb : a.row_end - 1;
   const int lim = a.causal ? min(a.Tk, a.km.count_le(qpos)) : a.Tk;
   const int wave_lim = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_first))) : a.Tk;
+  // keys past the wave's last row's limit are masked for all of its rows: the tiles from
+  // there on only keep the workgroup's barriers and loads going
+  const int wave_last = min(q0 + 32 * rb + 31, a.row_end - 1);
+  const int wave_end = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(wave_last))) : a.Tk;
 
   // ---- direct global -> LDS loads: the NL loader waves of a key share fill the 1 KB slots
   // of that share's tiles, loader lw the slots lw + NL*i (i < NIH). Slot position
@@ -398,16 +402,26 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
     step(j, sc, sn, T_{});
   };
   // two tiles per trip so that the score registers alternate instead of being copied
+  int n_jl = n_j;  // tiles of the share with a key below the wave's end
+  if constexpr (KS == 1) n_jl = min(n_j, (wave_end + kBN - 1) / kBN);
   int j = 0;
-  for (; j + 2 < n_j; j += 2) {
+  for (; j + 2 < n_jl; j += 2) {
     run(j, sA, sB);
     run(j + 1, sB, sA);
   }
-  if (j + 1 < n_j) {
+  if (j + 1 < n_jl) {
     run(j, sA, sB);
     step(j + 1, sB, sA, F_{});
-  } else if (j < n_j) {
+  } else if (j < n_jl) {
     step(j, sA, sB, F_{});
+  }
+  for (int jj = n_jl; jj < n_j; ++jj) {  // masked for every row of this wave
+    int later = 0;
+#pragma unroll
+    for (int g = 1; g <= NS - 2; ++g) later += group_units(jj + g);
+    wait_units<NIH>(later);
+    __syncthreads();
+    issue_group(jj + NS - 1);
   }
   for (int e = n_j; e < n_jmax; ++e) __syncthreads();  // a share with fewer tiles pads
 
