@@ -86,7 +86,11 @@ def parse():
     ap.add_argument("--separate-merge", action="store_true",
                     help="run the LSE merge as its own launch after each block forward (two-launch form)")
     ap.add_argument("--split-bwd", action="store_true",
-                    help="call the two halves of the block backward separately (per-half timings)")
+                    help="call the two halves of the block backward separately (per-half timings; the "
+                         "recomputing form)")
+    ap.add_argument("--recompute-bwd", action="store_true",
+                    help="at D = 128, the block backward without dS staging (the dQ kernel forms S and dP "
+                         "again)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch of the dominant kernel (from rocprofv3 --pmc)")
     return ap.parse_args()
@@ -158,6 +162,9 @@ class Share:
         self.bh = w.B * w.H
 
     split_bwd = False
+    # at D = 128 the block backward stages dS in HBM (cpattn_block_bwd_staged); False: the
+    # recomputing form (cpattn_block_bwd)
+    staged_bwd = True
     # ring steps after the first fold their rows into the running (O, LSE) in the block
     # kernel's epilogue (cpattn_block_fwd_merge); False: block output, then cpattn_lse_merge
     fused_merge = True
@@ -222,6 +229,13 @@ class Share:
                 plan.append(("lse_merge", (Tl - rb) * self.bh * (12 * D + 12), lib.cpattn_lse_merge,
                              (by(o), by(lse), by(ob), by(lb), B, H, Tl, D, rb, Tl, st)))
         if do_bwd:
+            stage = (0 if split_bwd or not self.staged_bwd else
+                     lib.cpattn_block_bwd_staged_workspace_bytes(B, H, Tl, Tk, D))
+            if stage:
+                import torch
+                if getattr(self, "ds_ws", None) is None or self.ds_ws.numel() < stage:
+                    self.ds_ws = torch.empty(stage, dtype=torch.uint8, device=self.q.device)
+                wsp = cp.ctypes.c_void_p(self.ds_ws.data_ptr())
             plan.append(("bwd_preprocess", self.bh * Tl * (D * 2 + D * 4 + 4), lib.cpattn_bwd_preprocess,
                          (by(do), bf16, by(o), by(delta), B, H, Tl, D, st)))
             for s, (src, rb, pairs) in enumerate(self.steps):
@@ -234,6 +248,12 @@ class Share:
                 if self.tab is not None:
                     # backward over the rotated rows kept from the forward
                     k, q = kr[src], qf
+                if stage:
+                    # dS of the dK/dV kernel staged in HBM and contracted by the dQ kernel
+                    plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd_staged,
+                                 (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
+                                  B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, acc, wsp, stage, st)))
+                    continue
                 if gqa:
                     plan.append(("block_bwd", 10 * D * pairs * self.bh, lib.cpattn_block_bwd_gqa,
                                  (by(q), by(k), by(v), by(do), bf16, by(lse), by(delta), by(dq), by(dk), by(dv),
@@ -590,9 +610,9 @@ def cpu_baseline(w, share, do_bwd, min_seconds=10.0, max_reps=8):
 
 COPY_BYTES = 512 << 20  # calibration copy for the HBM counters (twice the last-level cache)
 # GPU kernels behind each timed launch name (one dispatch of each per launch)
-GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dq_kernel"), "block_fwd": ("fwd_bf16_kernel",
-               "fwd_rope_kernel"), "block_fwd_merge": ("fwd_bf16_kernel",),
-               "block_bwd_dkdv": ("dkdv_kernel",), "block_bwd_dq": ("dq_kernel",),
+GPU_KERNELS = {"block_bwd": ("bwd_fused_kernel", "dkdv_kernel", "dkdv_pair_kernel", "dq_kernel", "dq_staged_kernel"),
+               "block_fwd": ("fwd_bf16_kernel", "fwd_rope_kernel"), "block_fwd_merge": ("fwd_bf16_kernel",),
+               "block_bwd_dkdv": ("dkdv_kernel", "dkdv_pair_kernel"), "block_bwd_dq": ("dq_kernel",),
                "lse_merge": ("merge_kernel",), "bwd_preprocess": ("delta_kernel",),
                "rope_rotate": ("rope_rotate_kernel",), "rope_rotate_grad": ("rope_rotate_grad_kernel",)}
 
@@ -633,6 +653,7 @@ def pmc_run(args):
     w = BY_NAME[args.workload]
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
+    share.staged_bwd = not args.recompute_bwd
     share.fused_merge = not args.separate_merge
     share.build_plan(_do_bwd(args, w))
     for _ in range(3):
@@ -702,7 +723,7 @@ def traffic_from(args):
 
 
 # the launch family with the largest time in each workload's step (the roofline's kernel)
-DOMINANT = {"win32k": "block_fwd", "win16k": "block_fwd", "gpt2s": "block_bwd", "bwd16k": "block_bwd_dkdv",
+DOMINANT = {"win32k": "block_fwd", "win16k": "block_fwd", "gpt2s": "block_bwd", "bwd16k": "block_bwd",
             "gqa16k": "block_bwd"}
 
 
@@ -734,13 +755,15 @@ def _kernels_brief(kern):
                 "frac": round(d["frac"], 4)} for n, d in kern.items()}
 
 
-def _describe(w, do_bwd, fused_merge=True):
+def _describe(w, do_bwd, fused_merge=True, staged=True):
     rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and the own K block rotated once per "
            f"step with cpattn_rope_rotate; the other block arrives rotated by its owner)") if w.rope_theta else ""
     gqa = f", grouped-query ({w.kv_heads} KV heads)" if w.kv_heads != w.H else ""
     merge = ("LSE merge in the block kernel's epilogue from step 1 on" if fused_merge
              else "block output then cpattn_lse_merge from step 1 on")
-    parts = f"forward (block fwd; {merge})" + (" and backward (preprocess + dK/dV + dQ)" if do_bwd else "")
+    bwd = (" and backward (preprocess; dK/dV, writing dS to HBM; dQ from that dS)" if w.D == 128 and staged
+           else " and backward (preprocess + dK/dV + dQ)")
+    parts = f"forward (block fwd; {merge})" + (bwd if do_bwd else "")
     return (f"{w.name}: rank 0 share of causal ring attention, HeadTail, B={w.B} H={w.H} D={w.D} T={w.T} "
             f"ring={w.ring}{gqa}{rot}, {parts}, all KV blocks resident")
 
@@ -763,6 +786,7 @@ def main():
     do_bwd = _do_bwd(args, w)
     share = Share(w, seed_do=w.seed + 1000)
     share.split_bwd = args.split_bwd
+    share.staged_bwd = not args.recompute_bwd
     share.fused_merge = not args.separate_merge
     wall, kern, graphed, n_warm = time_steps(share, args.steps, args.warmup, do_bwd=do_bwd, graph=not args.no_graph)
     flops = share.flops(do_bwd)
@@ -786,7 +810,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": _describe(w, do_bwd, share.fused_merge),
+        "config": {"workload": _describe(w, do_bwd, share.fused_merge, share.staged_bwd and not share.split_bwd),
                    "B": w.B, "H": w.H, "D": w.D, "T": w.T, "ring": w.ring, "rank": 0,
                    "rope_theta": w.rope_theta, "backward": do_bwd,
                    "causal_pairs_per_head": share.pairs, "flops_per_step": flops,
@@ -807,13 +831,13 @@ def main():
             if wx.name == w.name and bwd == do_bwd:
                 continue
             sx = Share(wx, seed_do=wx.seed + 1000)
-            sx.split_bwd = wx.D == 128  # at D = 128 the two halves are separate launches anyway
+            sx.staged_bwd = not args.recompute_bwd
             wl, kx, _, _ = time_steps(sx, EXTRA_STEPS, EXTRA_WARMUP, do_bwd=bwd)
             fl = sx.flops(bwd)
             key = name + ("_fwd_bwd" if name == w.name else "")
             extra[key] = {"ms_per_step": round(wl * 1e3, 3), "TFLOP/s": round(fl / wl / 1e12, 1),
                           "pct_bf16_peak": round(100 * fl / wl / 1e12 / PEAK_BF16_TFLOPS, 2),
-                          "parts": _describe(wx, bwd), "kernels": _kernels_brief(kx)}
+                          "parts": _describe(wx, bwd, staged=sx.staged_bwd), "kernels": _kernels_brief(kx)}
             if "block_fwd" in kx and name not in fwd_fracs:
                 fwd_fracs[name] = [round(kx[n]["frac"], 4) for n in ("block_fwd", "block_fwd_merge") if n in kx]
             del sx

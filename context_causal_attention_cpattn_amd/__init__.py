@@ -26,6 +26,7 @@ __all__ = [
     "cpattn_ring_fwd", "cpattn_bwd_preprocess", "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq",
     "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
     "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc", "NOALLOC_MAX_ROWS", "EXPORTS",
+    "cpattn_block_bwd_staged_workspace_bytes", "cpattn_block_bwd_staged", "cpattn_ring_bwd_staged_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +39,8 @@ EXPORTS = (
     "cpattn_lse_merge", "cpattn_ring_fwd_workspace_bytes", "cpattn_ring_fwd", "cpattn_bwd_preprocess",
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
     "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
-    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc",
+    "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc", "cpattn_block_bwd_staged_workspace_bytes",
+    "cpattn_block_bwd_staged", "cpattn_ring_bwd_staged_workspace_bytes",
 )
 
 NOALLOC_MAX_ROWS = 1 << 20  # CPATTN_NOALLOC_MAX_ROWS: B*H*Tq limit of cpattn_ring_bwd_noalloc
@@ -90,6 +92,10 @@ _SIGS = {
     "cpattn_block_fwd_merge": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32,
                                               _f32, _i64, _i64, _T, _T, _vp]),
     "cpattn_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
+    "cpattn_ring_bwd_staged_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "cpattn_block_bwd_staged_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
+    "cpattn_block_bwd_staged": (ctypes.c_int, [_T, _T, _T, _T, _i32, _T, _T, _T, _T, _T, _i64, _i64, _i64, _i64,
+                                               _i64, _i64, _M, _M, _i32, _f32, _i32, _vp, ctypes.c_size_t, _vp]),
     "cpattn_ring_bwd": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                        _f32, _T, _T, _T, _T, _T, _T, _i32, _vp, ctypes.c_size_t, _vp]),
     "cpattn_ring_bwd_noalloc": (ctypes.c_int, [_T, _T, _T, _M, _i32, _i32, _M, _i32, _i64, _i64, _i64, _i64, _i64,
@@ -326,6 +332,10 @@ def cpattn_ring_bwd_workspace_bytes(B: int, H: int, Tq: int) -> int:
     return int(load().cpattn_ring_bwd_workspace_bytes(B, H, Tq))
 
 
+def cpattn_ring_bwd_staged_workspace_bytes(B: int, H: int, Tq: int, Tk: int, D: int) -> int:
+    return int(load().cpattn_ring_bwd_staged_workspace_bytes(B, H, Tq, Tk, D))
+
+
 def cpattn_ring_bwd(q, k_blocks: Sequence, v_blocks: Sequence, kmaps: Sequence, rank: int, qmap, dout, o, lse, dq_acc,
                     dk_blocks: Sequence, dv_blocks: Sequence, workspace, causal: bool = True, scale: float = 0.0,
                     accumulate: bool = True, stream=None):
@@ -483,3 +493,29 @@ def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap
                                        _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc), _tensor(dv_acc), B, H,
                                        H_kv, Tq, Tk, D, _map(qmap), _map(kmap), int(causal), float(scale),
                                        int(accumulate), _stream(stream)))
+
+
+def cpattn_block_bwd_staged_workspace_bytes(B: int, H: int, Tq: int, Tk: int, D: int) -> int:
+    return int(load().cpattn_block_bwd_staged_workspace_bytes(B, H, Tq, Tk, D))
+
+
+def cpattn_block_bwd_staged(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, workspace,
+                            causal: bool = True, scale: float = 0.0, accumulate: bool = True, stream=None):
+    """Block backward with dS staged in ``workspace`` (a device tensor of at least
+    cpattn_block_bwd_staged_workspace_bytes bytes; None where that is 0): dQ reuses the dK/dV
+    kernel's dS. k / v may have fewer heads than q (grouped-query)."""
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v, None)
+    _expect("dout", dout, (B, H, Tq, D), q.dtype, q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    _expect("delta", delta, (B, H, Tq), _f32(), q)
+    _expect("dq_acc", dq_acc, (B, H, Tq, D), _f32(), q)
+    _expect("dk_acc", dk_acc, (B, H_kv, Tk, D), _f32(), q)
+    _expect("dv_acc", dv_acc, (B, H_kv, Tk, D), _f32(), q)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError(f"workspace: on {workspace.device}, expected {q.device}")
+    ws = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().cpattn_block_bwd_staged(_tensor(q), _tensor(k), _tensor(v), _tensor(dout), _dtype(q),
+                                          _tensor(lse, 3), _tensor(delta, 3), _tensor(dq_acc), _tensor(dk_acc),
+                                          _tensor(dv_acc), B, H, H_kv, Tq, Tk, D, _map(qmap), _map(kmap), int(causal),
+                                          float(scale), int(accumulate), ws, wsb, _stream(stream)))

@@ -334,7 +334,12 @@ struct DkdvPairLds {
   alignas(16) bf16x8 sx[kNW][2][2][64];  // [pair][from wave w / w + 4][8-value half][lane]
 };
 
-template <int D, int NS>
+// Chunk (16 bytes) of a staged dS block that holds half i of the 16 values of lane group h
+// and key k: chunk 64 i + 32 h + (k ^ 8 (i ^ h)). The XOR spreads the chunks that one
+// transposing read of the dQ kernel takes over all LDS banks.
+__device__ __forceinline__ int ds_chunk(int i, int h, int k) { return 64 * i + 32 * h + (k ^ (8 * (i ^ h))); }
+
+template <int D, int NS, bool STAGE>
 __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_kt, DkdvPairLds<D, NS>& sm) {
   using C = BCfg<D>;
   constexpr int NIP = kTile * C::CPR / (64 * kNW);  // direct loads per loader wave per tile (Q, dO each)
@@ -483,6 +488,21 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
     for (int r = 0; r < 16; ++r) {
       pa[r >> 3][r & 7] = (__bf16)p[r];
       dsa[r >> 3][r & 7] = (__bf16)(p[r] * (dpv[r] - D4[r >> 2][r & 3]));
+    }
+    if constexpr (STAGE) {
+      // this wave's 32 x 32 block of dS for the dQ kernel (value e of dsa[i]: row
+      // 16i + 8(e/4) + 4h + e%4 of the block, key lq), written past the caches (it is read
+      // once, by another kernel); blocks past the last row or key are not part of the
+      // staging area and are never read. The stores share the vector memory counter with the
+      // tile loads: since loads complete in issue order, a wait whose count has dropped by a
+      // tile's loads plus these stores still implies that the tile's loads completed.
+      const int qr0 = q0 + 32 * hb;
+      if (qr0 < a.Tq && kw0 < a.Tk) {
+        const int hq = kvh * a.G + it / n;
+        char* blk = (char*)a.ds + (((int64_t)(b * a.H + hq) * a.nqb + (qr0 >> 5)) * a.nkb + (kw0 >> 5)) * 2048;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) __builtin_nontemporal_store(dsa[i], (bf16x8*)(blk + 16 * ds_chunk(i, h, lq)));
+      }
     }
     // keep what this wave accumulates (P for dV, dS for dK); hand the other to the partner
     bf16x8 mine[2][2];  // [32-row block][8-value half]
@@ -836,16 +856,174 @@ __device__ __forceinline__ void dq_body(const BwdArgs& a, int Lg, int n_qt, DqLd
   }
 }
 
+// ------------------------------------------------------------------ dQ from staged dS
+template <int D, int NS, int NW>
+struct DqStagedLds {
+  alignas(1024) char sk[NS][kKB * BCfg<D>::ROWB];
+  alignas(1024) char sds[NS][NW][2048];  // each wave's dS block of the tile
+};
+
+// Workgroup Lg of the dQ grid (Lg = bh * n_qt + heavy-first query tile), 128-wide heads,
+// with the dS blocks the dK/dV kernel staged: per 32-key tile u, wave w takes its block of
+// 32 rows x 32 keys (2 KB, one contiguous stream per wave) and the shared K tile into LDS,
+// then dQ^T += K^T dS^T with both operands through the transposing LDS read. The operands
+// and the order of the products are those of dq_body's phase B.
+template <int D, int NS, int NW>
+__device__ __forceinline__ void dq_staged_body(const BwdArgs& a, int Lg, int n_qt, DqStagedLds<D, NS, NW>& sm) {
+  using C = BCfg<D>;
+  static_assert(D == 128, "staged dS: 128-wide heads");
+  static_assert(NS >= 2, "pipeline depth");
+  constexpr int ROWS = 32 * NW;                  // query rows per workgroup
+  constexpr int NIQ = kKB * C::CPR / (64 * NW);  // K loads per wave per tile
+  constexpr int kSlotRows = 64 * NW / C::CPR;    // rows between a lane's consecutive K slots
+  static_assert(NIQ >= 1 && kSlotRows % 16 == 0, "tile layout");
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, h = l >> 5, lq = l & 31;
+  const int bh = Lg / n_qt;
+  const int qt = n_qt - 1 - (Lg - bh * n_qt);
+  const int b = bh / a.H, hh = bh - b * a.H;
+  const int q0 = qt * ROWS;
+  const int w_row0 = q0 + 32 * w;
+
+  const int last_row = (q0 + ROWS < a.Tq ? q0 + ROWS : a.Tq) - 1;
+  const int n_vis = a.causal ? a.km.count_le(a.qm.pos(last_row)) : a.Tk;
+  const int n_kt = (n_vis + kKB - 1) / kKB;
+  if (n_kt == 0) {  // no key of this block is visible to these rows: nothing to add
+    const int row = w_row0 + lq;
+    if (!a.acc_q && row < a.Tq) {  // an overwrite writes zeros
+      float* o = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)row * a.dq_st;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(f32x4*)(o + 32 * db + 8 * g + 4 * h) = f32x4{};
+    }
+    return;
+  }
+  // tiles of this wave: the keys its last row sees (the dK/dV kernel wrote every such block);
+  // blocks of later tiles are re-reads of its last block and are not used
+  int n_kw = 0;
+  if (w_row0 < a.Tq) {
+    const int w_last = min(w_row0 + 31, a.Tq - 1);
+    const int w_vis = a.causal ? min(a.Tk, a.km.count_le(a.qm.pos(w_last))) : a.Tk;
+    n_kw = (w_vis + kKB - 1) / kKB;
+  }
+  const int qb = min(w_row0 >> 5, a.nqb - 1);  // a wave past the last row re-reads an in-range block
+  const char* ds_row = (const char*)a.ds + ((int64_t)(b * a.H + hh) * a.nqb + qb) * a.nkb * 2048;
+
+  const int kvh = hh / a.G;
+  const __bf16* kp = (const __bf16*)a.k.p + b * a.k.sb + kvh * a.k.sh;
+  const int ld_r0 = (64 * w + l) / C::CPR;
+  const int ld_col = ((l % C::CPR) ^ swz_mask<D>(ld_r0)) * 8;
+  const unsigned ko = (unsigned)((ld_r0 * a.k.st + ld_col) * 2);
+  auto issue_tile = [&](int u) {
+    const char* tb = (const char*)(kp + (int64_t)u * kKB * a.k.st);
+    char* dst = sm.sk[u % NS];
+    if (u * kKB + kKB <= a.Tk) {
+#pragma unroll
+      for (int i = 0; i < NIQ; ++i)
+        load_lds16(tb + (int64_t)kSlotRows * i * a.k.st * 2, ko, dst + (w + NW * i) * 1024);
+    } else {  // rows past the block repeat the last key (their dS is zero)
+#pragma unroll
+      for (int i = 0; i < NIQ; ++i) {
+        const int r = min(ld_r0 + kSlotRows * i, a.Tk - 1 - u * kKB);
+        load_lds16(tb, (unsigned)((r * a.k.st + ld_col) * 2), dst + (w + NW * i) * 1024);
+      }
+    }
+    const char* src = ds_row + (int64_t)min(u, n_kw > 0 ? n_kw - 1 : 0) * 2048;
+    load_lds16_nt(src, (unsigned)(16 * l), sm.sds[u % NS][w]);
+    load_lds16_nt(src + 1024, (unsigned)(16 * l), sm.sds[u % NS][w] + 1024);
+  };
+
+  const Offs<D> off(l);
+  // transposing reads of the dS block: lane l takes row (query) 16((l/16)%2) + l%16 of the
+  // wave's 32, keys 16t + 8hi + 4h + {0..3} (the key order of the K^T operand). Source lane
+  // s = l%16 addresses key 16t + 8hi + 4h + s/4, rows 16((l/16)%2) + 4(s%4) + {0..3}.
+  int dso[2][2];
+  {
+    const int s = l & 15, e = s >> 2, m = s & 3, G = (l >> 4) & 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) dso[t][hi] = 16 * ds_chunk(G, m & 1, 16 * t + 8 * hi + 4 * h + e) + 8 * (m >> 1);
+  }
+  f32x16 acc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) acc[db] = f32x16{};
+
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < n_kt) issue_tile(j);
+  for (int u = 0; u < n_kt; ++u) {
+    wait_tiles<NIQ + 2>(min(NS - 2, n_kt - 1 - u));
+    __syncthreads();  // tile u visible; every wave is done with tile u-1
+    if (u + NS - 1 < n_kt) issue_tile(u + NS - 1);
+    if (u < n_kw) {
+      const char* K = sm.sk[u % NS];
+      const char* S = sm.sds[u % NS][w];
+      bf16x8 dsb[2], kt8[C::NDB];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        dsb[t] = cat8(lds_read_tr4((const __bf16*)(S + dso[t][0])), lds_read_tr4((const __bf16*)(S + dso[t][1])));
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+        kt8[db] = cat8(lds_read_tr4((const __bf16*)(K + off.tro[0][db])), lds_read_tr4((const __bf16*)(K + off.tro[1][db])));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          acc[db] = mfma32(kt8[db], dsb[t], acc[db]);
+          if (t == 0)
+            kt8[db] = cat8(lds_read_tr4((const __bf16*)(K + 16 * C::ROWB + off.tro[0][db])),
+                           lds_read_tr4((const __bf16*)(K + 16 * C::ROWB + off.tro[1][db])));
+        }
+      }
+    }
+  }
+
+  {
+    const int wrows = min(32, a.Tq - w_row0);
+    float* base = a.dq + b * a.dq_sb + hh * a.dq_sh + (int64_t)w_row0 * a.dq_st;
+    const int bytes = wrows > 0 ? ((wrows - 1) * (int)a.dq_st + D) * 4 : 0;  // rows never overlap: st >= D
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, kBufferFlags);
+    const auto rl = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, a.acc_q ? bytes : 0, kBufferFlags);
+    auto offset = [&](int db, int g) { return (int)((lq * a.dq_st + 32 * db + 8 * g + 4 * h) * 4); };
+    u32x4 old[C::NDB][4];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) old[db][g] = __builtin_amdgcn_raw_buffer_load_b128(rl, offset(db, g), 0, 0);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = __builtin_bit_cast(f32x4, old[db][g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v4[j] += a.scale * acc[db][4 * g + j];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), rs, offset(db, g), 0, 0);
+      }
+  }
+}
+
+template <int D, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void dq_staged_kernel(BwdArgs a, int n_qt, int vary) {
+  __shared__ DqStagedLds<D, NS, NW> sm;
+  int head, rank;
+  xcd_tile(blockIdx.x, gridDim.x, n_qt, vary != 0, head, rank);
+  dq_staged_body<D, NS, NW>(a, head * n_qt + rank, n_qt, sm);
+}
+
 template <int D, int NS>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   __shared__ DkdvLds<D, NS> sm;
   dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
-template <int D, int NS>
+template <int D, int NS, bool STAGE>
 __global__ __launch_bounds__(64 * kPairWaves, 1) void dkdv_pair_kernel(BwdArgs a, int n_kt) {
   __shared__ DkdvPairLds<D, NS> sm;
-  dkdv_pair_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+  dkdv_pair_body<D, NS, STAGE>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
 template <int D, int NS, int KS>
@@ -907,10 +1085,27 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  // at D = 128, a causal block whose first and last row tiles see different numbers of keys
+  const int vary = D == 128 && a.causal &&
+                   a.km.count_le(a.qm.pos(std::min(kQPerWG, a.Tq) - 1)) != a.km.count_le(a.qm.pos(a.Tq - 1));
+  if constexpr (D == 128) {
+    if (which == 3 && a.ds) {  // dQ from the dS blocks the dK/dV kernel stages
+      constexpr int NSD = 6, NWD = 8;  // 256 rows per workgroup, 144 KB of LDS
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK, true>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0, s,
+                         a, n_kt);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int rows = 32 * NWD, n_qs = (a.Tq + rows - 1) / rows;
+      const int vary_s = a.causal && a.km.count_le(a.qm.pos(std::min(rows, a.Tq) - 1)) != a.km.count_le(a.qm.pos(a.Tq - 1));
+      hipLaunchKernelGGL((dq_staged_kernel<D, NSD, NWD>), dim3((unsigned)(bh * n_qs)), dim3(64 * NWD), 0, s, a, n_qs,
+                         vary_s);
+      return hipGetLastError();
+    }
+  }
   if (which & 1) {
     if constexpr (D == 128)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0, s, a,
-                         n_kt);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK, false>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0,
+                         s, a, n_kt);
     else
       hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
@@ -923,9 +1118,6 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
         return hipGetLastError();
       }
     }
-    // at D = 128, a causal block whose first and last row tiles see different numbers of keys
-    const int vary = D == 128 && a.causal &&
-                     a.km.count_le(a.qm.pos(std::min(kQPerWG, a.Tq) - 1)) != a.km.count_le(a.qm.pos(a.Tq - 1));
     hipLaunchKernelGGL((dq_kernel<D, NSQ, 1>), dim3((unsigned)(bh * n_qt)), dim3(64 * kNW), 0, s, a, n_qt, vary);
     return hipGetLastError();
   }

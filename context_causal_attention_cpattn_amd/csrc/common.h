@@ -118,6 +118,14 @@ __device__ __forceinline__ void load_lds16(const void* base, unsigned off, const
                : "memory", "m0");
 }
 
+// load_lds16 with the non-temporal hint, for data read once (streams that would otherwise
+// evict tiles the other workgroups of an XCD still re-read from its L2).
+__device__ __forceinline__ void load_lds16_nt(const void* base, unsigned off, const void* lds_wave_base) {
+  const unsigned lds = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+
 // Sum of the 8 bf16 values of v, added to acc (v_dot2 against (1, 1)).
 __device__ __forceinline__ float sum8_bf16(const bf16x8& v, float acc) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;

@@ -537,10 +537,44 @@ int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cp
                     scale, accumulate, 2, stream, "block_bwd_dq", H);
 }
 
+// Staging area of the dS blocks: one 2 KB block (32 query rows x 32 keys, bf16) per (b, query
+// head, 32-row block, 32-key block); 128-wide heads only.
+size_t cpattn_block_bwd_staged_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D) {
+  if (B <= 0 || H <= 0 || Tq <= 0 || Tk <= 0 || D != 128) return 0;
+  return ws_part((size_t)B * H * (size_t)((Tq + 31) / 32) * (size_t)((Tk + 31) / 32) * 2048);
+}
+
+int cpattn_block_bwd_staged(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                            const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                            const cpattn_tensor* delta, const cpattn_tensor* dq_acc, const cpattn_tensor* dk_acc,
+                            const cpattn_tensor* dv_acc, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                            int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                            float scale, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  BwdArgs a;
+  int st = build_bwd(a, q, k, v, dout, dtype, lse, delta, dq_acc, dk_acc, dv_acc, B, H, Tq, Tk, D, qmap, kmap,
+                     causal, scale, accumulate, accumulate, 3, H_kv);
+  if (st) return st;
+  const size_t need = cpattn_block_bwd_staged_workspace_bytes(B, H, Tq, Tk, D);
+  if (need) {
+    if (!workspace || workspace_bytes < need) return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");
+    a.ds = workspace;
+    a.nqb = (int)((Tq + 31) / 32);
+    a.nkb = (int)((Tk + 31) / 32);
+  }
+  return launch_status(launch_bwd_bf16(a, 3, (hipStream_t)stream), "block_bwd_staged");
+}
+
 // Workspace layout: [fp32 delta, B x H x Tq], 256-byte aligned.
 size_t cpattn_ring_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq) {
   if (B <= 0 || H <= 0 || Tq <= 0) return 0;
   return ws_part((size_t)B * H * Tq * 4);
+}
+
+// [fp32 delta | dS staging area of the largest block], both 256-byte aligned.
+size_t cpattn_ring_bwd_staged_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D) {
+  return cpattn_ring_bwd_workspace_bytes(B, H, Tq) + cpattn_block_bwd_staged_workspace_bytes(B, H, Tq, Tk, D);
 }
 
 int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const cpattn_tensor* v_blocks,
@@ -559,6 +593,9 @@ int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
   if (!workspace || workspace_bytes < need) return fail(CPATTN_EINVAL, "workspace of %zu bytes needed", need);
   if (((uintptr_t)workspace & 255u) != 0) return fail(CPATTN_EINVAL, "workspace not 256-byte aligned");
   const cpattn_tensor delta{workspace, H * Tq, Tq, 1};
+  // room for the dS staging area after delta: dQ reuses the dK/dV kernel's dS
+  const size_t stage = cpattn_block_bwd_staged_workspace_bytes(B, H, Tq, Tk, D);
+  void* ds = stage && workspace_bytes - need >= stage ? (void*)((char*)workspace + need) : nullptr;
   // validate every step before launching anything
   for (int32_t i = 0; i < ring; ++i) {
     BwdArgs a;
@@ -579,6 +616,7 @@ int cpattn_ring_bwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
     BwdArgs a;
     build_bwd(a, q, &k_blocks[src], &v_blocks[src], dout, dtype, lse, &delta, dq_acc, &dk_blocks[src],
               &dv_blocks[src], B, H, Tq, Tk, D, qmap, &kmaps[src], causal, scale, acc_q, accumulate, 3, H);
+    if (ds) a.ds = ds, a.nqb = (int)((Tq + 31) / 32), a.nkb = (int)((Tk + 31) / 32);
     hipError_t e = launch_bwd_bf16(a, 3, s);
     if (e != hipSuccess) return launch_status(e, "ring_bwd block");
   }

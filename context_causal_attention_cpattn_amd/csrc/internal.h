@@ -69,6 +69,13 @@ struct BwdArgs {
   // 1: add into the accumulator; 0: overwrite it (zeros where no pair contributes)
   int acc_q;   // dQ
   int acc_kv;  // dK and dV
+  // Staged dS (128-wide heads, both halves): the dK/dV kernel writes every visible dS block
+  // of 32 query rows x 32 keys (bf16, 2 KB) here and the dQ kernel contracts them with K
+  // instead of forming S and dP again. Block (b * H + h, qb, kb) starts at byte
+  // ((b * H + h) * nqb + qb) * nkb + kb) * 2048, nqb = ceil(Tq / 32), nkb = ceil(Tk / 32).
+  // Null: the dQ kernel recomputes dS.
+  void* ds;
+  int nqb, nkb;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

@@ -63,6 +63,8 @@ extern "C" int cpattn_ring_bwd_noalloc(const cpattn_tensor* q, const cpattn_tens
                             (long long)(B * H * Tq), kScratchRows);
   void* ws = nullptr;
   if (int st = scratch_address(&ws)) return st;
+  // exactly delta's share of the array: the dS staging of a larger workspace is never used here
   return cpattn_ring_bwd(q, k_blocks, v_blocks, kmaps, ring, rank, qmap, dtype, B, H, Tq, Tk, D, causal, scale, dout,
-                         o, lse, dq_acc, dk_blocks, dv_blocks, accumulate, ws, kScratchRows * sizeof(float), stream);
+                         o, lse, dq_acc, dk_blocks, dv_blocks, accumulate, ws, cpattn_ring_bwd_workspace_bytes(B, H, Tq),
+                         stream);
 }

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 6
+#define CPATTN_ABI_VERSION 7
 
 enum {
   CPATTN_OK = 0,
@@ -348,8 +348,37 @@ int cpattn_block_bwd_dq(const cpattn_tensor* q, const cpattn_tensor* k, const cp
                         const cpattn_posmap* kmap, int32_t causal, float scale, int32_t accumulate,
                         void* stream);
 
+/*
+ * Block backward with dS staged in HBM: cpattn_block_bwd_gqa (H_kv = H: cpattn_block_bwd)
+ * with the same arguments and accumulate semantics, for callers that can lend a workspace.
+ * At D = 128 the dK/dV kernel writes every visible block of dS = P * (dout v^T - delta)
+ * (bf16, the value its dK product uses) into the workspace, and the dQ kernel forms
+ * dq_acc += scale * dS k from those blocks instead of forming P and dS a second time: each
+ * of S, dP, dV, dK and dQ is computed once (the FA2 count of 10 D flops per visible pair,
+ * against 14 D for cpattn_block_bwd), for 4 bytes of HBM traffic per visible pair (the
+ * block written and read back). The dQ kernel contracts the same bf16 dS values in the same
+ * order as cpattn_block_bwd's dQ kernel. No atomics: bitwise reproducible.
+ * workspace: device memory of cpattn_block_bwd_staged_workspace_bytes(B,H,Tq,Tk,D) bytes,
+ * 256-byte aligned, owned by the caller; its contents on entry do not matter and on return
+ * are unspecified. At D = 64 that size is 0, workspace may be NULL, and the call is
+ * cpattn_block_bwd_gqa.
+ * Errors: as cpattn_block_bwd_gqa, plus EINVAL for a short or misaligned workspace.
+ */
+size_t cpattn_block_bwd_staged_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D);
+int cpattn_block_bwd_staged(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                            const cpattn_tensor* dout, int32_t dtype, const cpattn_tensor* lse,
+                            const cpattn_tensor* delta, const cpattn_tensor* dq_acc,
+                            const cpattn_tensor* dk_acc, const cpattn_tensor* dv_acc, int64_t B,
+                            int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
+                            const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal,
+                            float scale, int32_t accumulate, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Workspace bytes cpattn_ring_bwd needs: the fp32 delta of the local rows. 0 for non-positive sizes. */
 size_t cpattn_ring_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq);
+/* Workspace bytes with which cpattn_ring_bwd stages dS (delta, then the staging area of one
+ * block); equal to cpattn_ring_bwd_workspace_bytes where no staging applies (D != 128). */
+size_t cpattn_ring_bwd_staged_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D);
 
 /*
  * Ring backward of rank `rank` out of `ring`, all KV blocks resident in HBM:
@@ -373,7 +402,10 @@ size_t cpattn_ring_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq);
  * back with cpattn_rope_rotate_grad); o and lse are cpattn_ring_fwd's outputs.
  * Multi-head only (H_kv = H). ring + 1 launches at most, no synchronisation.
  * workspace: device memory of cpattn_ring_bwd_workspace_bytes(B,H,Tq) bytes,
- * 256-byte aligned.
+ * 256-byte aligned. With at least cpattn_ring_bwd_staged_workspace_bytes(B,H,Tq,Tk,D)
+ * bytes (D = 128), the workspace also holds the dS staging area of
+ * cpattn_block_bwd_staged and every step runs that form (same results, bit for bit;
+ * 2 ring + 1 launches at most).
  * Errors: as cpattn_block_bwd for any step (checked before any launch), plus
  * EINVAL for ring < 1, rank out of range, null block arrays, a short or
  * misaligned workspace.

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 6
+    assert cp.cpattn_version() == 7
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -149,6 +149,33 @@ def test_ring_bwd_workspace_size():
     assert cp.cpattn_ring_bwd_workspace_bytes(1, 16, 16384) == 16 * 16384 * 4
     assert cp.cpattn_ring_bwd_workspace_bytes(1, 1, 3) == 256
     assert cp.cpattn_ring_bwd_workspace_bytes(0, 1, 1) == 0
+
+
+def test_staged_workspace_sizes():
+    # one 2 KB block (32 rows x 32 keys, bf16) per (b, head, row block, key block), 128-wide heads only
+    assert cp.cpattn_block_bwd_staged_workspace_bytes(1, 32, 8192, 8192, 128) == 32 * 256 * 256 * 2048
+    assert cp.cpattn_block_bwd_staged_workspace_bytes(2, 3, 33, 1, 128) == 2 * 3 * 2 * 1 * 2048
+    assert cp.cpattn_block_bwd_staged_workspace_bytes(1, 1, 64, 64, 64) == 0
+    assert cp.cpattn_block_bwd_staged_workspace_bytes(0, 1, 64, 64, 128) == 0
+    assert cp.cpattn_ring_bwd_staged_workspace_bytes(1, 16, 16384, 16384, 128) == (
+        16 * 16384 * 4 + 16 * 512 * 512 * 2048)
+    assert cp.cpattn_ring_bwd_staged_workspace_bytes(1, 2, 100, 100, 64) == cp.cpattn_ring_bwd_workspace_bytes(1, 2, 100)
+
+
+def test_block_bwd_staged_rejects_before_launch():
+    lib = cp.load()
+    m = cp.cpattn_posmap(64, 64, 0, 0)
+    t, l3, t4 = _t(st=128), _t(st=1), _t(st=128)
+    bt, bm, bl, b4 = ctypes.byref(t), ctypes.byref(m), ctypes.byref(l3), ctypes.byref(t4)
+    need = cp.cpattn_block_bwd_staged_workspace_bytes(1, 2, 64, 64, 128)
+    assert need == 2 * 2 * 2 * 2048
+    call = lambda ws=ctypes.c_void_p(0x100000), wsb=need, D=128, dtype=1, H_kv=2: lib.cpattn_block_bwd_staged(
+        bt, bt, bt, bt, dtype, bl, bl, b4, b4, b4, 1, 2, H_kv, 64, 64, D, bm, bm, 1, 0.0, 1, ws, wsb, None)
+    assert call(ws=None, wsb=0) == -1 and "workspace" in cp.cpattn_last_error()
+    assert call(wsb=need - 1) == -1 and "workspace" in cp.cpattn_last_error()
+    assert call(ws=ctypes.c_void_p(0x100010)) == -1 and "aligned" in cp.cpattn_last_error()
+    assert call(dtype=0) == -2  # fp32 backward, found before the workspace
+    assert call(H_kv=3) == -1   # H not a multiple of H_kv
 
 
 def test_block_fwd_merge_rejects_before_launch():

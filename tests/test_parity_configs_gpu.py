@@ -47,15 +47,24 @@ class Share:
         cp.cpattn_ring_fwd(self.q, self.kb, self.vb, self.maps, self.rank, self.maps[self.rank], self.o, self.lse,
                            self.ws, rope_table=self.tab)
 
-    def backward(self, dk, dv, dq=None):
+    def backward(self, dk, dv, dq=None, staged=False):
+        """Per-step block backward calls; ``staged``: the form that stages dS in HBM."""
         w, N, r = self.w, self.w.ring, self.rank
         self.delta = torch.empty(w.B, w.H, w.local_len, device=DEV)
         cp.cpattn_bwd_preprocess(self.do, self.o, self.delta)
         self.dq = torch.zeros_like(self.o) if dq is None else dq
+        ws = None
+        if staged:
+            n = cp.cpattn_block_bwd_staged_workspace_bytes(w.B, w.H, w.local_len, w.local_len, w.D)
+            ws = torch.full((max(n, 1),), 0xFF, dtype=torch.uint8, device=DEV)  # NaN where never written
         for s in range(N):
             src = (r - s) % N
-            cp.cpattn_block_bwd(self.q, self.kb[src], self.vb[src], self.do, self.lse, self.delta, self.dq, dk[src],
-                                dv[src], self.maps[r], self.maps[src])
+            args = (self.q, self.kb[src], self.vb[src], self.do, self.lse, self.delta, self.dq, dk[src], dv[src],
+                    self.maps[r], self.maps[src])
+            if staged:
+                cp.cpattn_block_bwd_staged(*args, ws)
+            else:
+                cp.cpattn_block_bwd(*args)
 
 
 def oracle_fwd(t, rows, heads, rope_theta=0.0):
@@ -185,6 +194,17 @@ def test_bwd16k_all_ranks():
         s.forward()
         s.backward(dk, dv)
         shares.append(s)
+    # the form with dS staged in HBM gives the same bits on every head of both ranks
+    dk2 = [torch.zeros_like(x) for x in dk]
+    dv2 = [torch.zeros_like(x) for x in dk]
+    for s in shares:
+        dq1 = s.dq
+        s.backward(dk2, dv2, staged=True)
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, s.dq), s.rank
+    for r in range(w.ring):
+        assert torch.equal(dk[r], dk2[r]) and torch.equal(dv[r], dv2[r]), r
+    log("  staged dS: every head of both ranks bitwise equal to the recomputing form")
     torch.cuda.synchronize()
     heads = [0, 11, 20, 31]
     res = per_head(lambda h: oa.causal_attention_bwd(*(f64(t[n][:, h:h + 1]) for n in ("q", "k", "v", "do"))),
@@ -277,9 +297,11 @@ def test_win32k_rope_backward_all_ranks_sampled():
     assert rk <= 1e-3 and rv <= 1e-3
 
 
-def _ring_bwd(s, dq, dk, dv, accumulate):
+def _ring_bwd(s, dq, dk, dv, accumulate, staged=False):
     w = s.w
-    ws = torch.empty(cp.cpattn_ring_bwd_workspace_bytes(w.B, w.H, w.local_len), dtype=torch.uint8, device=DEV)
+    n = (cp.cpattn_ring_bwd_staged_workspace_bytes(w.B, w.H, w.local_len, w.local_len, w.D) if staged
+         else cp.cpattn_ring_bwd_workspace_bytes(w.B, w.H, w.local_len))
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)
     cp.cpattn_ring_bwd(s.q, s.kb, s.vb, s.maps, s.rank, s.maps[s.rank], s.do, s.o, s.lse, dq, dk, dv, ws,
                        accumulate=accumulate)
 
@@ -302,12 +324,13 @@ def test_ring_bwd_equals_step_driven_backward(name, rank):
     dv_ref = [torch.zeros(shape, device=DEV) for _ in range(w.ring)]
     s.backward(dk_ref, dv_ref)
     nan = lambda: torch.full(shape, float("nan"), device=DEV)
-    dq, dk, dv = nan(), [nan() for _ in range(w.ring)], [nan() for _ in range(w.ring)]
-    _ring_bwd(s, dq, dk, dv, accumulate=False)
-    torch.cuda.synchronize()
-    assert torch.equal(dq, s.dq)
-    for i in range(w.ring):
-        assert torch.equal(dk[i], dk_ref[i]) and torch.equal(dv[i], dv_ref[i]), i
+    for staged in (False, True):  # with room to stage dS: the same bits
+        dq, dk, dv = nan(), [nan() for _ in range(w.ring)], [nan() for _ in range(w.ring)]
+        _ring_bwd(s, dq, dk, dv, accumulate=False, staged=staged)
+        torch.cuda.synchronize()
+        assert torch.equal(dq, s.dq), staged
+        for i in range(w.ring):
+            assert torch.equal(dk[i], dk_ref[i]) and torch.equal(dv[i], dv_ref[i]), (i, staged)
     # accumulate: both forms start from the same fill
     g = torch.Generator(device="cpu").manual_seed(7)
     fill = [torch.randn(shape, generator=g).to(DEV) for _ in range(1 + 2 * w.ring)]
