@@ -323,15 +323,14 @@ __device__ __forceinline__ void dkdv_body(const BwdArgs& a, int Lg, int n_kt, Dk
 // tile has landed; the exchanged halves are in LDS. Only waves 0-3 issue the tile loads.
 // The arithmetic of every product and of dS is that of dkdv_body, so the results are the
 // same bits.
-constexpr int kPairWaves = 8;
 
-template <int D, int NS>
+template <int D, int NS, int NP>
 struct DkdvPairLds {
   alignas(1024) char sq[NS][BCfg<D>::TILEB];
   alignas(1024) char sdo[NS][BCfg<D>::TILEB];
   alignas(16) float slse[NS][kTile];
   alignas(16) float sdelta[NS][kTile];
-  alignas(16) bf16x8 sx[kNW][2][2][64];  // [pair][from wave w / w + 4][8-value half][lane]
+  alignas(16) bf16x8 sx[NP][2][2][64];  // [pair][from wave w / w + NP][8-value half][lane]
 };
 
 // Chunk (16 bytes) of a staged dS block that holds half i of the 16 values of lane group h
@@ -339,24 +338,25 @@ struct DkdvPairLds {
 // transposing read of the dQ kernel takes over all LDS banks.
 __device__ __forceinline__ int ds_chunk(int i, int h, int k) { return 64 * i + 32 * h + (k ^ (8 * (i ^ h))); }
 
-template <int D, int NS, bool STAGE>
-__device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_kt, DkdvPairLds<D, NS>& sm) {
+template <int D, int NS, int NP, bool STAGE>
+__device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_kt, DkdvPairLds<D, NS, NP>& sm) {
   using C = BCfg<D>;
-  constexpr int NIP = kTile * C::CPR / (64 * kNW);  // direct loads per loader wave per tile (Q, dO each)
-  static_assert(NIP >= 1, "tile layout");
+  constexpr int NIP = kTile * C::CPR / (64 * NP);  // direct loads per loader wave per tile (Q, dO each)
+  constexpr int RL = kTile / NP;                   // rows of LSE and delta a loader wave brings
+  static_assert(NIP >= 1 && (NP == 2 || NP == 4), "tile layout");
   auto& sq = sm.sq;
   auto& sdo = sm.sdo;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, h = l >> 5, lq = l & 31;
-  const int hb = w >= kNW ? 1 : 0;  // 32-row block of each tile this wave forms; 0: keeps dV
-  const int kw = w & (kNW - 1);
+  const int hb = w >= NP ? 1 : 0;  // 32-row block of each tile this wave forms; 0: keeps dV
+  const int kw = w & (NP - 1);
   const int bh = Lg / n_kt;  // (b, KV head)
   const int kt = Lg - bh * n_kt;
   const int H_kv = a.H / a.G;
   const int b = bh / H_kv, kvh = bh - b * H_kv;
-  const int kc0 = kt * kKeysPerWG;  // first key of the workgroup
+  const int kc0 = kt * 32 * NP;  // first key of the workgroup
   const int kw0 = kc0 + 32 * kw;    // first key of the pair
   const int key = kw0 + lq;         // this lane's key
   const bool key_ok = key < a.Tk;
@@ -381,9 +381,10 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
     qo[i] = (unsigned)((ld_row[i] * a.q.st + ld_col[i]) * 2);
     oo[i] = (unsigned)((ld_row[i] * a.dout.st + ld_col[i]) * 2);
   }
-  // Only the dV waves (0-3) load the tiles: the dK waves go straight from the barrier to
-  // their products while the loads queue (a loader brings 16 rows of Q, dO, LSE and delta)
-  const int sr = 16 * kw + (l & 15);
+  // Only the dV waves (0 .. NP-1) load the tiles: the dK waves go straight from the barrier
+  // to their products while the loads queue (a loader brings 64 / NP rows of Q, dO, LSE and
+  // delta)
+  const int sr = RL * kw + (l % RL);
   auto issue_tile = [&](int it, int buf) {
     if (hb != 0) return;
     const int hq = kvh * a.G + it / n;
@@ -407,10 +408,10 @@ __device__ __forceinline__ void dkdv_pair_body(const BwdArgs& a, int Lg, int n_k
       load_lds16(qbase, q_off, sq[buf] + (kw * NIP + i) * 1024);
       load_lds16(obase, o_off, sdo[buf] + (kw * NIP + i) * 1024);
     }
-    if (l < 16) {
+    if (l < RL) {
       const int r = tail ? min(sr, a.Tq - 1 - q0) : sr;
-      load_lds4(lp + (int64_t)q0 * a.lse.st, (unsigned)(r * a.lse.st * 4), &sm.slse[buf][16 * kw]);
-      load_lds4(dp + (int64_t)q0 * a.delta.st, (unsigned)(r * a.delta.st * 4), &sm.sdelta[buf][16 * kw]);
+      load_lds4(lp + (int64_t)q0 * a.lse.st, (unsigned)(r * a.lse.st * 4), &sm.slse[buf][RL * kw]);
+      load_lds4(dp + (int64_t)q0 * a.delta.st, (unsigned)(r * a.delta.st * 4), &sm.sdelta[buf][RL * kw]);
     }
   };
 
@@ -1020,10 +1021,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdArgs a, int n_kt) {
   dkdv_body<D, NS>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
-template <int D, int NS, bool STAGE>
-__global__ __launch_bounds__(64 * kPairWaves, 1) void dkdv_pair_kernel(BwdArgs a, int n_kt) {
-  __shared__ DkdvPairLds<D, NS> sm;
-  dkdv_pair_body<D, NS, STAGE>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
+template <int D, int NS, int NP, bool STAGE>
+__global__ __launch_bounds__(128 * NP, 4 / NP) void dkdv_pair_kernel(BwdArgs a, int n_kt) {
+  __shared__ DkdvPairLds<D, NS, NP> sm;
+  dkdv_pair_body<D, NS, NP, STAGE>(a, xcd_remap(blockIdx.x, gridDim.x), n_kt, sm);
 }
 
 template <int D, int NS, int KS>
@@ -1064,6 +1065,9 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   constexpr int NSK = D == 64 ? 4 : 3;  // dK/dV: stages of 64 query rows
   constexpr int NSQ = 4;                // dQ: stages of 32 keys
   const int n_kt = (a.Tk + kKeysPerWG - 1) / kKeysPerWG;
+  // 128-wide heads: pairs of waves per dK/dV workgroup (32 keys each) and its Q/dO stages
+  constexpr int NPP = 4, NSP = NPP == 4 ? 3 : 2;
+  const int n_ktp = (a.Tk + 32 * NPP - 1) / (32 * NPP);
   const int n_qt = (a.Tq + kQPerWG - 1) / kQPerWG;
   const int64_t bh = (int64_t)a.B * a.H;           // (b, query head) for dQ
   const int64_t bkv = (int64_t)a.B * (a.H / a.G);  // (b, KV head) for dK / dV
@@ -1091,8 +1095,8 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   if constexpr (D == 128) {
     if (which == 3 && a.ds) {  // dQ from the dS blocks the dK/dV kernel stages
       constexpr int NSD = 6, NWD = 8;  // 256 rows per workgroup, 144 KB of LDS
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK, true>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0, s,
-                         a, n_kt);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSP, NPP, true>), dim3((unsigned)(bkv * n_ktp)), dim3(128 * NPP), 0,
+                         s, a, n_ktp);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       const int rows = 32 * NWD, n_qs = (a.Tq + rows - 1) / rows;
@@ -1104,8 +1108,8 @@ hipError_t launch_d(const BwdArgs& a, int which, hipStream_t s) {
   }
   if (which & 1) {
     if constexpr (D == 128)
-      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSK, false>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kPairWaves), 0,
-                         s, a, n_kt);
+      hipLaunchKernelGGL((dkdv_pair_kernel<D, NSP, NPP, false>), dim3((unsigned)(bkv * n_ktp)), dim3(128 * NPP), 0,
+                         s, a, n_ktp);
     else
       hipLaunchKernelGGL((dkdv_kernel<D, NSK>), dim3((unsigned)(bkv * n_kt)), dim3(64 * kNW), 0, s, a, n_kt);
     hipError_t e = hipGetLastError();
