@@ -191,17 +191,23 @@ class Share:
         keep = [q, do, o, lse, ob, lb, delta, dq, qm]
         plan = []
         qf = q
+        rotq = False  # the block kernels rotate the Q rows as they load them
         if self.tab is not None:
             tab, rows = cp.ctypes.c_void_p(self.tab.data_ptr()), self.tab.shape[0]
-            qf = T(self.q_rot)
             kr = [T(x) for x in self.k_rot]
-            keep += [qf] + kr
+            keep += kr
             # x read + out written (bf16), the table row of each position once
             rot_bytes = B * H * Tl * 4 * D + Tl * 4 * D
             k0, km0 = T(self.kb[0]), cp._map(self.maps[0])
             keep += [k0, km0]
-            plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
-                         (by(q), bf16, B, H, Tl, D, by(qm), tab, rows, by(qf), st)))
+            if do_bwd:
+                # the backward takes the rotated Q rows: rotate them once, for both passes
+                qf = T(self.q_rot)
+                keep.append(qf)
+                plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
+                             (by(q), bf16, B, H, Tl, D, by(qm), tab, rows, by(qf), st)))
+            else:
+                rotq = True
             plan.append(("rope_rotate", rot_bytes, lib.cpattn_rope_rotate,
                          (by(k0), bf16, B, H, Tk, D, by(km0), tab, rows, by(kr[0]), st)))
         for s, (src, rb, pairs) in enumerate(self.steps):
@@ -212,12 +218,21 @@ class Share:
             if self.tab is not None:
                 k = kr[src]  # rotated once by its owner
             if s > 0 and self.fused_merge:
+                if rotq:
+                    plan.append(("block_fwd_merge", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_rotq,
+                                 (by(q), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, tab, rows,
+                                  rb, Tl, 1, by(o), by(lse), st)))
+                    continue
                 plan.append(("block_fwd_merge", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_merge,
                              (by(qf), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, rb, Tl,
                               by(o), by(lse), st)))
                 continue
             oo, ll = (o, lse) if s == 0 else (ob, lb)
-            if gqa:
+            if rotq:
+                plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_rotq,
+                             (by(q), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, tab, rows,
+                              0 if s == 0 else rb, Tl, 0, by(oo), by(ll), st)))
+            elif gqa:
                 plan.append(("block_fwd", 4 * D * pairs * self.bh, lib.cpattn_block_fwd_gqa,
                              (by(qf), by(k), by(v), bf16, B, H, Hkv, Tl, Tk, D, by(qm), by(km), 1, 0.0, None, 0,
                               0 if s == 0 else rb, Tl, by(oo), by(ll), st)))
@@ -756,8 +771,15 @@ def _kernels_brief(kern):
 
 
 def _describe(w, do_bwd, fused_merge=True, staged=True):
-    rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and the own K block rotated once per "
-           f"step with cpattn_rope_rotate; the other block arrives rotated by its owner)") if w.rope_theta else ""
+    if not w.rope_theta:
+        rot = ""
+    elif do_bwd:
+        rot = (f", rotary theta {w.rope_theta:g} at global positions (Q and the own K block rotated once per "
+               f"step with cpattn_rope_rotate; the other block arrives rotated by its owner)")
+    else:
+        rot = (f", rotary theta {w.rope_theta:g} at global positions (the own K block rotated once per step "
+               f"with cpattn_rope_rotate, the Q rows by the block kernels as they load them; the other block "
+               f"arrives rotated by its owner)")
     gqa = f", grouped-query ({w.kv_heads} KV heads)" if w.kv_heads != w.H else ""
     merge = ("LSE merge in the block kernel's epilogue from step 1 on" if fused_merge
              else "block output then cpattn_lse_merge from step 1 on")

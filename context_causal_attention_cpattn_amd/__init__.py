@@ -27,6 +27,7 @@ __all__ = [
     "cpattn_step_rows", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
     "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc", "NOALLOC_MAX_ROWS", "EXPORTS",
     "cpattn_block_bwd_staged_workspace_bytes", "cpattn_block_bwd_staged", "cpattn_ring_bwd_staged_workspace_bytes",
+    "cpattn_block_fwd_rotq",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +41,7 @@ EXPORTS = (
     "cpattn_block_bwd", "cpattn_block_bwd_dkdv", "cpattn_block_bwd_dq", "cpattn_step_rows", "cpattn_rope_rotate",
     "cpattn_rope_rotate_grad", "cpattn_block_fwd_gqa", "cpattn_block_bwd_gqa", "cpattn_ring_bwd_workspace_bytes",
     "cpattn_ring_bwd", "cpattn_block_fwd_merge", "cpattn_ring_bwd_noalloc", "cpattn_block_bwd_staged_workspace_bytes",
-    "cpattn_block_bwd_staged", "cpattn_ring_bwd_staged_workspace_bytes",
+    "cpattn_block_bwd_staged", "cpattn_ring_bwd_staged_workspace_bytes", "cpattn_block_fwd_rotq",
 )
 
 NOALLOC_MAX_ROWS = 1 << 20  # CPATTN_NOALLOC_MAX_ROWS: B*H*Tq limit of cpattn_ring_bwd_noalloc
@@ -91,6 +92,8 @@ _SIGS = {
                                            _i32, _f32, _i32, _vp]),
     "cpattn_block_fwd_merge": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32,
                                               _f32, _i64, _i64, _T, _T, _vp]),
+    "cpattn_block_fwd_rotq": (ctypes.c_int, [_T, _T, _T, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _M, _M, _i32,
+                                             _f32, _vp, _i64, _i64, _i64, _i32, _T, _T, _vp]),
     "cpattn_ring_bwd_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "cpattn_ring_bwd_staged_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
     "cpattn_block_bwd_staged_workspace_bytes": (ctypes.c_size_t, [_i64, _i64, _i64, _i64, _i64]),
@@ -477,6 +480,24 @@ def cpattn_block_fwd_merge(q, k, v, qmap, kmap, o_acc, lse_acc, causal: bool = T
     _check(load().cpattn_block_fwd_merge(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
                                          _map(qmap), _map(kmap), int(causal), float(scale), row_begin, row_end,
                                          _tensor(o_acc), _tensor(lse_acc, 3), _stream(stream)))
+
+
+def cpattn_block_fwd_rotq(q, k, v, qmap, kmap, o, lse, rope_table, causal: bool = True, scale: float = 0.0,
+                          row_begin: int = 0, row_end: int | None = None, merge: bool = False, stream=None):
+    """Block forward with the Q rows rotated at their global positions as they are loaded (k arrives
+    rotated); merge: fold into the running (o, lse) instead of writing them. k / v may have fewer
+    heads than q (grouped-query)."""
+    B, H, H_kv, Tq, Tk, D = _inputs(q, k, v)
+    _expect("o", o, (B, H, Tq, D), _f32(), q)
+    _expect("lse", lse, (B, H, Tq), _f32(), q)
+    if rope_table is None:
+        raise ValueError("rope_table is required")
+    _rope_check(rope_table, D, q)
+    rp, rr = _rope_args(rope_table)
+    row_end = Tq if row_end is None else row_end
+    _check(load().cpattn_block_fwd_rotq(_tensor(q), _tensor(k), _tensor(v), _dtype(q), B, H, H_kv, Tq, Tk, D,
+                                        _map(qmap), _map(kmap), int(causal), float(scale), rp, rr, row_begin, row_end,
+                                        int(merge), _tensor(o), _tensor(lse, 3), _stream(stream)))
 
 
 def cpattn_block_bwd_gqa(q, k, v, dout, lse, delta, dq_acc, dk_acc, dv_acc, qmap, kmap, causal: bool = True,

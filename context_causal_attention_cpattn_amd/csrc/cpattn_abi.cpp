@@ -271,6 +271,24 @@ int cpattn_block_fwd_merge(const cpattn_tensor* q, const cpattn_tensor* k, const
   return launch_status(launch_fwd_bf16(a, (hipStream_t)stream), "block_fwd_merge");
 }
 
+int cpattn_block_fwd_rotq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v, int32_t dtype,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk, int64_t D,
+                          const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32_t causal, float scale,
+                          const float* rope_table, int64_t rope_rows, int64_t row_begin, int64_t row_end,
+                          int32_t merge, const cpattn_tensor* o, const cpattn_tensor* lse, void* stream) {
+  FwdArgs a{};
+  int G;
+  if (!rope_table) return fail(CPATTN_EINVAL, "rope table is NULL");
+  int st = build_fwd(a, q, k, v, dtype, B, H, Tq, Tk, D, qmap, kmap, causal, scale, rope_table, rope_rows,
+                     row_begin, row_end, o, lse);
+  if (st || (st = group_of(H, H_kv, &G))) return st;
+  if (merge != 0 && merge != 1) return fail(CPATTN_EINVAL, "merge must be 0 or 1");
+  a.G = G;
+  a.rope_q = 1;
+  a.merge = merge;
+  return launch_status(launch_fwd_bf16(a, (hipStream_t)stream), "block_fwd_rotq");
+}
+
 int cpattn_lse_merge(const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, const cpattn_tensor* o_blk,
                      const cpattn_tensor* lse_blk, int64_t B, int64_t H, int64_t T, int64_t D, int64_t row_begin,
                      int64_t row_end, void* stream) {
@@ -310,14 +328,14 @@ int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32
   return ok();
 }
 
-// Workspace layout: [fp32 block O][fp32 block LSE] and, with a rotary table,
-// [rotated Q][rotated K block] in bf16; every part 256-byte aligned.
+// Workspace layout: [fp32 block O][fp32 block LSE] and, with a rotary table, the
+// rotated K block in bf16; every part 256-byte aligned.
 static size_t ws_part(size_t b) { return (b + 255) / 256 * 256; }
 
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D, int32_t rope) {
   if (B <= 0 || H <= 0 || Tq <= 0 || Tk <= 0 || D <= 0) return 0;
   size_t n = ws_part((size_t)B * H * Tq * D * 4) + ws_part((size_t)B * H * Tq * 4);
-  if (rope) n += ws_part((size_t)B * H * Tq * D * 2) + ws_part((size_t)B * H * Tk * D * 2);
+  if (rope) n += ws_part((size_t)B * H * Tk * D * 2);
   return n;
 }
 
@@ -337,9 +355,9 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
                         rope_table, rope_rows, 0, Tq, o_acc, lse_acc)))
       return st;
   }
-  // With a rotary table and bf16 inputs, Q is rotated once and each K block once per
-  // step into the workspace, and the blocks run without rotation: every key is then
-  // rotated once instead of once per query tile.
+  // With a rotary table and bf16 inputs, each K block is rotated once per step into the
+  // workspace (every key rotated once instead of once per query tile) and the block kernel
+  // rotates the Q rows as it loads them into registers.
   const bool pre = rope_table != nullptr && dtype == CPATTN_BF16;
   const size_t need = cpattn_ring_fwd_workspace_bytes(B, H, Tq, Tk, D, pre ? 1 : 0);
   // bf16 steps merge in the block kernel's epilogue: only fp32 rings and rotary use the workspace
@@ -351,18 +369,16 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
   char* wp = (char*)workspace;
   float* o_ws = (float*)wp;
   float* l_ws = (float*)(wp + ws_part((size_t)B * H * Tq * D * 4));
-  __bf16* q_rot = (__bf16*)(wp + ws_part((size_t)B * H * Tq * D * 4) + ws_part((size_t)B * H * Tq * 4));
-  __bf16* k_rot = (__bf16*)((char*)q_rot + ws_part((size_t)B * H * Tq * D * 2));
+  __bf16* k_rot = (__bf16*)(wp + ws_part((size_t)B * H * Tq * D * 4) + ws_part((size_t)B * H * Tq * 4));
   cpattn_tensor o_blk{o_ws, H * Tq * D, Tq * D, D};
   cpattn_tensor l_blk{l_ws, H * Tq, Tq, 1};
-  const cpattn_tensor q_r{q_rot, H * Tq * D, Tq * D, D};
   const cpattn_tensor k_r{k_rot, H * Tk * D, Tk * D, D};
   hipStream_t s = (hipStream_t)stream;
-  if (pre) {
-    if ((st = cpattn_rope_rotate(q, dtype, B, H, Tq, D, qmap, rope_table, rope_rows, &q_r, stream))) return st;
-    q = &q_r;
-  }
   const float* blk_rope = pre ? nullptr : rope_table;
+  // the rotation of Q on load, for the block launches of a pre-rotated ring
+  auto rotate_q = [&](FwdArgs& a) {
+    if (pre) a.rope = rope_table, a.rope_rows = (int)rope_rows, a.rope_q = 1;
+  };
   // the K block a step uses: rotated into the workspace first when pre-rotating
   auto key_block = [&](int32_t src) -> const cpattn_tensor* {
     if (!pre) return &k_blocks[src];
@@ -382,6 +398,7 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
       FwdArgs a{};
       build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, blk_rope, rope_rows, 0, Tq,
                 o_acc, lse_acc);
+      rotate_q(a);
       hipError_t e = dtype == CPATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
       if (e != hipSuccess) return launch_status(e, "ring_fwd step 0");
       continue;
@@ -395,6 +412,7 @@ int cpattn_ring_fwd(const cpattn_tensor* q, const cpattn_tensor* k_blocks, const
       FwdArgs a{};
       build_fwd(a, q, kb, &v_blocks[src], dtype, B, H, Tq, Tk, D, qmap, km, causal, scale, nullptr, 0, rb, Tq,
                 o_acc, lse_acc);
+      rotate_q(a);
       a.merge = 1;
       hipError_t e = launch_fwd_bf16(a, s);
       if (e != hipSuccess) return launch_status(e, "ring_fwd block merge");

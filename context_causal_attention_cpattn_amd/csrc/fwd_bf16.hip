@@ -95,7 +95,7 @@ __device__ __forceinline__ void wait_units(int units) {
 //
 // NW is the number of waves of a workgroup (4: two workgroups per CU, 8: one).
 // With SPLIT_LOAD only the upper half of a key share's waves issue its tile loads.
-template <int D, int NS, int KS, int NW, bool SPLIT_LOAD>
+template <int D, int NS, int KS, int NW, bool SPLIT_LOAD, bool ROTQ>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, int n_qt, int vary) {
   using C = Cfg<D>;
   static_assert(NS >= 2 && NS <= 4, "pipeline depth");
@@ -135,6 +135,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
     qf[c] = __builtin_bit_cast(bf16x8, t);
   }
   const int qpos = a.qm.pos(row_ok ? row : a.row_end - 1);
+  if constexpr (ROTQ) {
+    // rotary at the row's global position: d and d + D/2 are a pair, both in this lane
+    // (chunks c and c + NC/2); the rounding of every kernel that rotates
+    if (row_ok) {
+      const float* tb = a.rope + (int64_t)qpos * D;
+#pragma unroll
+      for (int c = 0; c < C::NC / 2; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = 16 * c + 8 * h + e;
+          const float cs = tb[2 * i], sn = tb[2 * i + 1];
+          const float x1 = (float)qf[c][e], x2 = (float)qf[c + C::NC / 2][e];
+          qf[c][e] = (__bf16)rot_lo(x1, x2, cs, sn);
+          qf[c + C::NC / 2][e] = (__bf16)rot_hi(x1, x2, cs, sn);
+        }
+      }
+    }
+  }
   // Make the Q loads complete here, before the key loop: otherwise the compiler
   // waits for them inside the loop, where the wait would also cover the
   // in-flight LDS loads of later tiles.
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
   }
 }
 
-template <int D>
+template <int D, bool ROTQ>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   const int rows = a.row_end - a.row_begin;
   const int64_t bh = (int64_t)a.B * a.H;
@@ -519,7 +537,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     // a causal block whose first and last row tiles see different numbers of keys
     const int first_last = std::min(a.row_begin + 32 * NW, a.row_end) - 1;
     const int vary = a.causal && a.km.count_le(a.qm.pos(first_last)) != a.km.count_le(a.qm.pos(a.row_end - 1));
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1, NW, true>), dim3((unsigned)(n_qt * bh)), dim3(64 * NW), 0, s, a,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 1, NW, true, ROTQ>), dim3((unsigned)(n_qt * bh)), dim3(64 * NW), 0, s, a,
                        n_qt, vary);
     return hipGetLastError();
   } else {
@@ -527,12 +545,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
     // fewer than two workgroups per CU: split each workgroup's keys between two wave pairs
     if (grid1 < 512) {
       const int n_qt = (rows + kBM / 2 - 1) / (kBM / 2);
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2, kNW, false>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s,
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, 2, 2, kNW, false, ROTQ>), dim3((unsigned)(n_qt * bh)), dim3(64 * kNW), 0, s,
                          a, n_qt, 0);
       return hipGetLastError();
     }
     const int n_qt = (rows + kBM - 1) / kBM;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1, kNW, false>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, 4, 1, kNW, false, ROTQ>), dim3((unsigned)grid1), dim3(64 * kNW), 0, s, a, n_qt,
                        0);
     return hipGetLastError();
   }
@@ -541,8 +559,9 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.rope != nullptr) return launch_fwd_rope_bf16(a, s);
-  return a.D == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+  if (a.rope != nullptr && !a.rope_q) return launch_fwd_rope_bf16(a, s);
+  if (a.rope != nullptr) return a.D == 64 ? launch_d<64, true>(a, s) : launch_d<128, true>(a, s);
+  return a.D == 64 ? launch_d<64, false>(a, s) : launch_d<128, false>(a, s);
 }
 
 }  // namespace cpattn

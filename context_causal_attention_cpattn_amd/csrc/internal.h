@@ -25,6 +25,9 @@ struct FwdArgs {
   float scale;
   const float* rope;  // [rope_rows][D/2][2] or null
   int rope_rows;
+  // with rope: 0 rotates Q and K inside the kernel (K per tile); 1 rotates only the Q rows,
+  // as they are loaded into registers (K arrives rotated by its owner)
+  int rope_q;
   int row_begin, row_end;
   int G;  // query heads per KV head: query head h reads K and V head h / G
   int merge;  // 1: fold the block result into (o, lse) as the log-sum-exp merge does; 0: write it

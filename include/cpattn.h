@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 7
+#define CPATTN_ABI_VERSION 8
 
 enum {
   CPATTN_OK = 0,
@@ -214,6 +214,28 @@ int cpattn_block_fwd_merge(const cpattn_tensor* q, const cpattn_tensor* k, const
                            const cpattn_tensor* o_acc, const cpattn_tensor* lse_acc, void* stream);
 
 /*
+ * Block forward (merge = 0, as cpattn_block_fwd_gqa into o, lse) or block
+ * forward fused with the merge (merge = 1, as cpattn_block_fwd_merge into the
+ * running o, lse) whose Q rows are rotated at their global positions (qmap)
+ * with the rotary table as the kernel loads them into registers; k arrives
+ * already rotated, as its owner rotates a block once and sends it (BluScriptCP
+ * log, 2026-06-29 and 2026-07-10: rotary at global positions). The rotation is
+ * that of cpattn_rope_rotate, so the results equal cpattn_rope_rotate of q
+ * followed by the plain call bit for bit, without the pass over Q in HBM.
+ * bf16 inputs only; the table as in cpattn_block_fwd (it must cover every
+ * position of both maps).
+ * Errors: as cpattn_block_fwd_gqa (merge = 0) or cpattn_block_fwd_merge
+ * (merge = 1); EINVAL for a NULL table or merge outside {0, 1}; EUNSUPPORTED
+ * for fp32 inputs.
+ */
+int cpattn_block_fwd_rotq(const cpattn_tensor* q, const cpattn_tensor* k, const cpattn_tensor* v,
+                          int32_t dtype, int64_t B, int64_t H, int64_t H_kv, int64_t Tq, int64_t Tk,
+                          int64_t D, const cpattn_posmap* qmap, const cpattn_posmap* kmap,
+                          int32_t causal, float scale, const float* rope_table, int64_t rope_rows,
+                          int64_t row_begin, int64_t row_end, int32_t merge, const cpattn_tensor* o,
+                          const cpattn_tensor* lse, void* stream);
+
+/*
  * Step classification (host only, integer, exact): the local query rows that
  * see at least one key of a KV block. Positions increase with the local
  * index, so they form the suffix [*row_begin, qmap->len); *visible_keys is the
@@ -232,8 +254,8 @@ int cpattn_step_rows(const cpattn_posmap* qmap, const cpattn_posmap* kmap, int32
 
 /*
  * Workspace bytes cpattn_ring_fwd needs: an fp32 block output and LSE, and
- * with rope != 0 (a rotary table with bf16 inputs) room for the rotated Q and
- * one rotated K block. 0 for non-positive sizes.
+ * with rope != 0 (a rotary table with bf16 inputs) room for one rotated K
+ * block. 0 for non-positive sizes.
  */
 size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t Tk, int64_t D,
                                        int32_t rope);
@@ -249,9 +271,9 @@ size_t cpattn_ring_fwd_workspace_bytes(int64_t B, int64_t H, int64_t Tq, int64_t
  * launch), with fp32 inputs into the workspace and then by cpattn_lse_merge.
  * Steps whose block is invisible to every row are skipped. At most two
  * launches per step, no synchronisation. With a rotary
- * table and bf16 inputs, Q is rotated once (cpattn_rope_rotate) and each step
- * first rotates its K block into the workspace, then runs the block without
- * rotation (one more launch per step).
+ * table and bf16 inputs, each step first rotates its K block into the
+ * workspace (cpattn_rope_rotate, one more launch per step), then runs the block
+ * with its Q rows rotated as they are loaded (cpattn_block_fwd_rotq).
  * workspace: device memory of cpattn_ring_fwd_workspace_bytes(B,H,Tq,Tk,D,
  * rope) bytes, 256-byte aligned; used by fp32 rings (ring > 1) and by the
  * rotary form, may be NULL otherwise (bf16 without rotary, or ring == 1).

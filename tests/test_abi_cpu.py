@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version():
-    assert cp.cpattn_version() == 7
+    assert cp.cpattn_version() == 8
 
 
 @pytest.mark.parametrize("T,ring", [(8, 2), (256, 2), (4096, 4), (16384, 2), (32768, 2), (48, 3), (10, 5), (2, 1)])
@@ -178,6 +178,22 @@ def test_block_bwd_staged_rejects_before_launch():
     assert call(H_kv=3) == -1   # H not a multiple of H_kv
 
 
+def test_block_fwd_rotq_rejects_before_launch():
+    lib = cp.load()
+    m = cp.cpattn_posmap(64, 64, 0, 0)
+    t, l3 = _t(), _t(st=1)
+    bt, bm, bl = ctypes.byref(t), ctypes.byref(m), ctypes.byref(l3)
+    tab = ctypes.c_void_p(0x20000)
+    call = lambda dtype=1, H_kv=2, merge=0, rope=tab, rows=64: lib.cpattn_block_fwd_rotq(
+        bt, bt, bt, dtype, 1, 2, H_kv, 64, 64, 64, bm, bm, 1, 0.0, rope, rows, 0, 64, merge, bt, bl, None)
+    assert call(rope=None) == -1 and "table" in cp.cpattn_last_error()
+    assert call(rows=32) == -1 and "rotary table" in cp.cpattn_last_error()  # positions beyond the table
+    assert call(rope=ctypes.c_void_p(0x20004)) == -1                           # misaligned table
+    assert call(dtype=0) == -2                                                 # fp32 with rotary
+    assert call(merge=2) == -1 and "merge" in cp.cpattn_last_error()
+    assert call(H_kv=3) == -1
+
+
 def test_block_fwd_merge_rejects_before_launch():
     lib = cp.load()
     m = cp.cpattn_posmap(64, 64, 0, 0)
@@ -194,10 +210,11 @@ def test_block_fwd_merge_rejects_before_launch():
 def test_ring_workspace_size():
     assert cp.cpattn_ring_fwd_workspace_bytes(1, 32, 8192, 128) == 32 * 8192 * 128 * 4 + 32 * 8192 * 4
     assert cp.cpattn_ring_fwd_workspace_bytes(0, 1, 1, 1) == 0
-    # with rotary: rotated Q and one rotated K block in bf16, each part 256-byte aligned
+    # with rotary: one rotated K block in bf16 (Q is rotated as the block kernel loads it),
+    # each part 256-byte aligned
     base = cp.cpattn_ring_fwd_workspace_bytes(1, 16, 16384, 128)
-    assert cp.cpattn_ring_fwd_workspace_bytes(1, 16, 16384, 128, rope=True) == base + 2 * 16 * 16384 * 128 * 2
-    assert cp.cpattn_ring_fwd_workspace_bytes(1, 1, 3, 64, Tk=5, rope=True) == 768 + 256 + 512 + 768
+    assert cp.cpattn_ring_fwd_workspace_bytes(1, 16, 16384, 128, rope=True) == base + 16 * 16384 * 128 * 2
+    assert cp.cpattn_ring_fwd_workspace_bytes(1, 1, 3, 64, Tk=5, rope=True) == 768 + 256 + 768
 
 
 def test_ring_fwd_rotary_needs_workspace_even_alone():

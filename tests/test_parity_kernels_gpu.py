@@ -809,3 +809,52 @@ def test_gqa_with_group_one_is_bitwise_mha():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (4, 2)])
+def test_block_fwd_rotq_equals_rotate_then_block(D, H, H_kv):
+    """Q rows rotated as the block kernel loads them give the bits of cpattn_rope_rotate of Q
+    followed by the plain block forward (write, and merge into a running result), and the
+    oracle's rotary attention."""
+    log(f"block_fwd_rotq D={D} H={H} H_kv={H_kv}")
+    T, N = 1040, 2
+    B = 1
+    (qm, qp), (km1, kp1) = cp.cpattn_headtail_shard(T, N, 0), cp.cpattn_headtail_shard(T, N, 1)
+    Tl = T // N
+    q, = draw_shape(B, H, Tl, D, torch.bfloat16, seed=900 + D, n=1)
+    k0, v0, k1, v1 = draw_shape(B, H_kv, Tl, D, torch.bfloat16, seed=901 + D, n=4)
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    qd = q.to(DEV)
+    q_rot = torch.empty_like(qd)
+    cp.cpattn_rope_rotate(qd, qm, tab, out=q_rot)
+    k0r, k1r = torch.empty_like(k0.to(DEV)), torch.empty_like(k1.to(DEV))
+    cp.cpattn_rope_rotate(k0.to(DEV), qm, tab, out=k0r)
+    cp.cpattn_rope_rotate(k1.to(DEV), km1, tab, out=k1r)
+    v0d, v1d = v0.to(DEV), v1.to(DEV)
+    rb, _ = cp.cpattn_step_rows(qm, km1)
+    outs = []
+    for rot in (False, True):
+        o = torch.full((B, H, Tl, D), float("nan"), device=DEV)
+        lse = torch.full((B, H, Tl), float("nan"), device=DEV)
+        if rot:
+            cp.cpattn_block_fwd_rotq(qd, k0r, v0d, qm, qm, o, lse, tab)
+            cp.cpattn_block_fwd_rotq(qd, k1r, v1d, qm, km1, o, lse, tab, row_begin=rb, merge=True)
+        else:
+            cp.cpattn_block_fwd_gqa(q_rot, k0r, v0d, qm, qm, o, lse)
+            cp.cpattn_block_fwd_merge(q_rot, k1r, v1d, qm, km1, o, lse, row_begin=rb)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # against the oracle: rotary at the global positions, then causal attention over both blocks
+    G = H // H_kv
+    kk = np.concatenate([np.repeat(f64(k0), G, axis=1), np.repeat(f64(k1), G, axis=1)], axis=2)
+    vv = np.concatenate([np.repeat(f64(v0), G, axis=1), np.repeat(f64(v1), G, axis=1)], axis=2)
+    kpos = np.concatenate([positions(qm), positions(km1)])
+    qr = orope.rope_apply(f64(q), positions(qm), 10000.0)
+    kr = orope.rope_apply(kk, kpos, 10000.0)
+    O, L = oa.block_attention_fwd(qr, kr, vv, positions(qm), kpos, causal=True)
+    eo, el = max_err(f64(outs[1][0]), O), max_err(f64(outs[1][1]), L)
+    log(f"  max err O {eo:.3g} LSE {el:.3g}")
+    assert max(eo, el) <= TOL_BF16
