@@ -389,3 +389,48 @@ def test_ring_bwd_contiguous_shards_with_invisible_blocks():
                      max_err(f64(dk2[src]) - 3.0, gk[:, :, p]), max_err(f64(dv2[src]) - 3.0, gv[:, :, p])]
         log(f"  rank {rank}: max err {max(errs):.3g}")
         assert max(errs) <= TOL_BF16
+
+
+def test_gqa16k_staged_backward_bitwise_both_ranks():
+    """The grouped-query 16k workload (32 query heads over 8 KV heads) at full size: the staged
+    block backward gives the bits of the recomputing one for every step of both ranks (dQ per
+    query head, dK/dV summed over each group), with the staging area filled with NaN."""
+    w = BY_NAME["gqa16k"]
+    log(f"workload {w.name}")
+    t = draw(w)
+    N, Tl, Hk = w.ring, w.local_len, w.kv_heads
+    maps, pos = zip(*[cp.cpattn_headtail_shard(w.T, N, r) for r in range(N)])
+    kb = [gather(t["k"], p) for p in pos]
+    vb = [gather(t["v"], p) for p in pos]
+    n = cp.cpattn_block_bwd_staged_workspace_bytes(w.B, w.H, Tl, Tl, w.D)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)
+    for r in range(N):
+        q, do = gather(t["q"], pos[r]), gather(t["do"], pos[r])
+        o = torch.empty(w.B, w.H, Tl, w.D, device=DEV)
+        lse = torch.empty(w.B, w.H, Tl, device=DEV)
+        cp.cpattn_block_fwd_gqa(q, kb[r], vb[r], maps[r], maps[r], o, lse)
+        for s in range(1, N):
+            src = (r - s) % N
+            rb, _ = cp.cpattn_step_rows(maps[r], maps[src])
+            if rb < Tl:
+                cp.cpattn_block_fwd_merge(q, kb[src], vb[src], maps[r], maps[src], o, lse, row_begin=rb)
+        delta = torch.empty(w.B, w.H, Tl, device=DEV)
+        cp.cpattn_bwd_preprocess(do, o, delta)
+        res = []
+        for staged in (False, True):
+            dq = torch.zeros(w.B, w.H, Tl, w.D, device=DEV)
+            dk = [torch.zeros(w.B, Hk, Tl, w.D, device=DEV) for _ in range(N)]
+            dv = [torch.zeros_like(x) for x in dk]
+            for s in range(N):
+                src = (r - s) % N
+                args = (q, kb[src], vb[src], do, lse, delta, dq, dk[src], dv[src], maps[r], maps[src])
+                if staged:
+                    cp.cpattn_block_bwd_staged(*args, ws, accumulate=s > 0)
+                else:
+                    cp.cpattn_block_bwd_gqa(*args, accumulate=s > 0)
+            res.append([dq] + dk + dv)
+        torch.cuda.synchronize()
+        for x, y in zip(*res):
+            assert torch.equal(x, y), r
+            assert bool(torch.isfinite(y).all()), r
+        log(f"  rank {r}: staged equals recomputing on dQ and every block's dK, dV")

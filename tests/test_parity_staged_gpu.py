@@ -164,3 +164,43 @@ def test_ring_bwd_staged_workspace_bitwise(T, N):
         torch.cuda.synchronize()
         for x, y in zip(*res):
             assert torch.equal(x, y), r
+
+
+def test_block_bwd_staged_strided_views():
+    """Inputs and accumulators that are views into larger allocations (head and row strides
+    beyond their shapes): the staged form still equals the recomputing one bit for bit."""
+    B, H, Tq, Tk, D = 2, 3, 180, 200, 128
+    log("block_bwd_staged strided")
+    g = torch.Generator(device="cpu").manual_seed(77)
+
+    def view(shape, pad_h=1, pad_t=24, dtype=torch.bfloat16):
+        Bb, Hh, T, Dd = shape
+        big = (torch.randn(Bb, Hh + pad_h, T + pad_t, Dd + 64, generator=g) * 0.7).to(dtype).to(DEV)
+        return big[:, :Hh, :T, :Dd]
+
+    q, do = view((B, H, Tq, D)), view((B, H, Tq, D))
+    k, v = view((B, H, Tk, D)), view((B, H, Tk, D))
+    qm, km = (Tq, Tq, 0, 0), (Tk, Tk, 0, 0)
+    O, L = oa.block_attention_fwd(f64(q), f64(k), f64(v), positions(qm), positions(km), causal=True)
+    o = torch.tensor(O, dtype=torch.float32, device=DEV)
+    lse = torch.tensor(L, dtype=torch.float32, device=DEV)
+    delta = torch.empty(B, H, Tq, device=DEV)
+    cp.cpattn_bwd_preprocess(do, o, delta)
+    outs = []
+    for staged in (False, True):
+        acc = [view((B, H, Tq, D), dtype=torch.float32), view((B, H, Tk, D), dtype=torch.float32),
+               view((B, H, Tk, D), dtype=torch.float32)]
+        for x in acc:
+            x.zero_()
+        if staged:
+            ws = nan_area(cp.cpattn_block_bwd_staged_workspace_bytes(B, H, Tq, Tk, D))
+            cp.cpattn_block_bwd_staged(q, k, v, do, lse, delta, *acc, qm, km, ws)
+        else:
+            cp.cpattn_block_bwd(q, k, v, do, lse, delta, *acc, qm, km)
+        outs.append(acc)
+    torch.cuda.synchronize()
+    for x, y in zip(*outs):
+        assert torch.equal(x, y)
+    gq, gk, gv = oa.block_attention_bwd(f64(q), f64(k), f64(v), f64(do), O, L, positions(qm), positions(km))
+    for t_, r in zip(outs[1], (gq, gk, gv)):
+        assert max_err(f64(t_), r) <= tol_bf16_scaled(r)
