@@ -21,7 +21,7 @@
 //     and the K/V bytes loaded per flop are half those of two 4-wave workgroups;
 //   * scores are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16,
 //     so every lane holds 16 scores of ONE query row per 32-key block: the row
-//     max is an in-lane max3 chain plus one exchange with lane l^32, and the row
+//     max is an in-lane max3 chain plus one swap with lane l^32, and the row
 //     sum stays a per-lane partial until the epilogue;
 //   * the output is accumulated transposed, O^T += V^T P^T: P comes straight
 //     from the score registers (same lane = same query), and V^T is read from
@@ -45,6 +45,20 @@
 
 namespace cpattn {
 namespace {
+
+// Max / sum of a lane's value and that of lane l ^ 32. v_permlane32_swap (a vector ALU
+// op, no LDS round trip) swaps the upper 32 lanes of its first operand with the lower 32
+// of its second; with the same value in both, every lane gets its own value in one
+// result and lane l ^ 32's in the other. Max and sum are symmetric in the two, so both
+// halves of the wave end with the same bits.
+__device__ __forceinline__ float xor32_max(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float m) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 constexpr int kNW = 4;          // waves per workgroup at D = 64
 constexpr int kBM = 32 * kNW;   // query rows per workgroup at D = 64
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, sA[kb][r]);
-    mx = fmaxf(m, __shfl_xor(m, 32));
+    mx = xor32_max(m);
   }
 
   // Tile j of this wave's share. `sc` holds its S (masked) and `mx` its row max on entry;
@@ -410,7 +424,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
             m2 = fmaxf(m2, sn[kb][r]);
           }
       }
-      mx = fmaxf(m2, __shfl_xor(m2, 32));
+      mx = xor32_max(m2);
     }
   };
 
@@ -474,7 +488,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(FwdArgs a, in
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2; with a.merge the row is folded into
   // the running (O, LSE) instead, with the arithmetic of the merge kernel (merge.hip)
-  const float l_tot = l_part + __shfl_xor(l_part, 32);
+  const float l_tot = xor32_sum(l_part);
   if (row_ok) {
     const bool live = l_tot > 0.f;
     const float inv = live ? 1.f / l_tot : 0.f;
