@@ -507,6 +507,19 @@ def test_bwd_sum_identities():
     np.testing.assert_allclose(dv.sum(axis=-2), do.sum(axis=-2), atol=1e-12)
 
 
+def test_bwd_scale_symmetry():
+    # S depends on q and k only through q.k: the output is unchanged under q -> a q, k -> k / a,
+    # so d/da at a = 1 gives sum_p q_p.dQ_p = sum_j k_j.dK_j (per head, causal or not)
+    q, k, v, do = rnd(2, 40, 8, seed=96), rnd(2, 40, 8, seed=97), rnd(2, 40, 8, seed=98), rnd(2, 40, 8, seed=99)
+    dq, dk, _, _, _ = attention.causal_attention_bwd(q, k, v, do)
+    lhs, rhs = (q * dq).sum(axis=(-2, -1)), (k * dk).sum(axis=(-2, -1))
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    # the GPU tests check this at full size on every head: a dQ off by 1 % on one row breaks it
+    bad = dq.copy()
+    bad[1, 17] *= 1.01
+    assert np.abs((q * bad).sum(axis=(-2, -1)) - rhs).max() > 1e-6 * np.abs(q * dq).sum()
+
+
 @pytest.mark.parametrize("ring_n", [2, 3])
 def test_bwd_ring_accumulated_equals_unsharded(ring_n):
     # dev log 2026-06-05: the two-rank ring gradient equals the single-pass gradient.

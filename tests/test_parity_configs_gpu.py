@@ -4,8 +4,10 @@ backward per ring step), against the fp64 oracle.
 
 The kernels always run on every head. The forward of every workload is
 compared on every head; the 16k backward on four heads spread over the grid
-(first, last and two between), both ranks, every row and key of those heads.
-The oracle runs one head per host thread.
+(first, last and two between), both ranks, every row and key of those heads,
+and on every head through sums the softmax fixes (sum of dK zero, sum of dV
+the sum of dO, sum q.dQ equal to sum k.dK). The oracle runs one head per host
+thread.
 """
 import numpy as np
 import pytest
@@ -219,6 +221,31 @@ def test_bwd16k_all_ranks():
         ev = max_err(f64(dv[s.rank][:, heads]), dV[:, :, rows])
         log(f"  rank {s.rank}, heads {heads}: O {eo:.3g} LSE {el:.3g} dq {eq:.3g} dk {ek:.3g} dv {ev:.3g}")
         assert max(eo, el, eq, ek, ev) <= TOL_BF16
+    _bwd_sum_invariants(w, t, shares, dk, dv)
+
+
+def _bwd_sum_invariants(w, t, shares, dk, dv):
+    """Every head, every row and key of the sequence: each row of P sums to one and each row
+    of dS to zero, so sum_j dV_j = sum_p dO_p and sum_j dK_j = 0; and S depends on q and k
+    only through q.k, so scaling q by a and k by 1/a changes nothing: sum_p q_p.dQ_p =
+    sum_j k_j.dK_j (both sides contract the same dS values, so this one holds to fp32
+    accumulation)."""
+    g = lambda x: torch.empty(w.B, w.H, w.T, w.D, dtype=torch.float64, device=DEV)
+    dqg, dkg, dvg = g(0), g(0), g(0)
+    for s in shares:
+        dqg[:, :, list(s.pos[s.rank])] = s.dq.double()
+    for r in range(w.ring):
+        idx = list(shares[0].pos[r])
+        dkg[:, :, idx] = dk[r].double()
+        dvg[:, :, idx] = dv[r].double()
+    qg, kg, dog = (t[n].to(DEV).double() for n in ("q", "k", "do"))
+    rk = float((dkg.sum(2).abs() / dkg.abs().sum(2)).max())
+    rv = float(((dvg.sum(2) - dog.sum(2)).abs() / dvg.abs().sum(2)).max())
+    qd, kd = qg * dqg, kg * dkg
+    rs = float(((qd.sum((2, 3)) - kd.sum((2, 3))).abs() / (qd.abs().sum((2, 3)) + kd.abs().sum((2, 3)))).max())
+    log(f"  every head: |sum dK| / sum|dK| {rk:.3g}, |sum dV - sum dO| / sum|dV| {rv:.3g}, "
+        f"|sum q.dQ - sum k.dK| / sum|.| {rs:.3g}")
+    assert rk <= 1e-3 and rv <= 1e-3 and rs <= 1e-6
 
 
 def test_win32k_rope_backward_all_ranks_sampled():
@@ -434,3 +461,22 @@ def test_gqa16k_staged_backward_bitwise_both_ranks():
             assert torch.equal(x, y), r
             assert bool(torch.isfinite(y).all()), r
         log(f"  rank {r}: staged equals recomputing on dQ and every block's dK, dV")
+        _local_sum_invariants(q, do, res[1][0], kb, res[1][1:1 + N], res[1][1 + N:], w.H // Hk)
+
+
+def _local_sum_invariants(q, do, dq, kbs, dks, dvs, G):
+    """One rank's rows against every key block, per KV head (grouped-query: G query heads
+    share it): the identities of the full-size backward above, restricted to the rows this
+    rank holds (each row's P and dS rows run over all keys of all blocks)."""
+    B, H, _, D = q.shape
+    qd = (q.double() * dq.double()).reshape(B, H // G, G, -1, D)
+    dog = do.double().reshape(B, H // G, G, -1, D).sum((2, 3))
+    dk = torch.cat([x.double() for x in dks], dim=2)
+    dv = torch.cat([x.double() for x in dvs], dim=2)
+    kd = torch.cat([x.double() for x in kbs], dim=2) * dk
+    rk = float((dk.sum(2).abs() / dk.abs().sum(2)).max())
+    rv = float(((dv.sum(2) - dog).abs() / dv.abs().sum(2)).max())
+    rs = float(((qd.sum((2, 3, 4)) - kd.sum((2, 3))).abs() / (qd.abs().sum((2, 3, 4)) + kd.abs().sum((2, 3)))).max())
+    log(f"  every KV head: |sum dK| / sum|dK| {rk:.3g}, |sum dV - sum dO| / sum|dV| {rv:.3g}, "
+        f"|sum q.dQ - sum k.dK| / sum|.| {rs:.3g}")
+    assert rk <= 1e-3 and rv <= 1e-3 and rs <= 1e-6
