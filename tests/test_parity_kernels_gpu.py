@@ -858,3 +858,42 @@ def test_block_fwd_rotq_equals_rotate_then_block(D, H, H_kv):
     eo, el = max_err(f64(outs[1][0]), O), max_err(f64(outs[1][1]), L)
     log(f"  max err O {eo:.3g} LSE {el:.3g}")
     assert max(eo, el) <= TOL_BF16
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_block_fwd_rotq_row_range_and_non_causal(D):
+    """Rotate-on-load over a row range that starts and ends inside tiles (rows 37..454 of 520),
+    causal and not, written and merged: the bits of rotate-then-forward over the same range,
+    and the rows outside the range untouched."""
+    log(f"block_fwd_rotq row range D={D}")
+    T, N, B, H = 1040, 2, 1, 2
+    (qm, _), (km, _) = cp.cpattn_headtail_shard(T, N, 0), cp.cpattn_headtail_shard(T, N, 1)
+    Tl = T // N
+    q, k, v = (x.to(DEV) for x in draw_shape(B, H, Tl, D, torch.bfloat16, seed=950 + D, n=3))
+    tab = torch.empty(T, D, device=DEV)
+    cp.cpattn_rope_table(10000.0, T, D, tab)
+    q_rot, k_rot = torch.empty_like(q), torch.empty_like(k)
+    cp.cpattn_rope_rotate(q, qm, tab, out=q_rot)
+    cp.cpattn_rope_rotate(k, km, tab, out=k_rot)
+    r0, r1 = 37, 455
+    for causal in (True, False):
+        outs = []
+        for rot in (False, True):
+            o = torch.full((B, H, Tl, D), 7.0, device=DEV)
+            lse = torch.full((B, H, Tl), 3.0, device=DEV)
+            for merge in (False, True):
+                if rot:
+                    cp.cpattn_block_fwd_rotq(q, k_rot, v, qm, km, o, lse, tab, causal=causal, row_begin=r0,
+                                             row_end=r1, merge=merge)
+                elif merge:
+                    cp.cpattn_block_fwd_merge(q_rot, k_rot, v, qm, km, o, lse, causal=causal, row_begin=r0,
+                                              row_end=r1)
+                else:
+                    cp.cpattn_block_fwd_gqa(q_rot, k_rot, v, qm, km, o, lse, causal=causal, row_begin=r0,
+                                            row_end=r1)
+            outs.append((o, lse))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1]), causal
+        o, lse = outs[1]
+        assert bool((o[:, :, :r0] == 7.0).all() and (o[:, :, r1:] == 7.0).all())
+        assert bool((lse[:, :, :r0] == 3.0).all() and (lse[:, :, r1:] == 3.0).all())
