@@ -107,3 +107,15 @@ def test_headline_is_the_32k_window_forward():
     assert bench.HEADLINE == "win32k"
     assert not bench._do_bwd(args, BY_NAME["win32k"]) and bench._do_bwd(args, BY_NAME["gpt2s"])
     assert bench.DOMINANT["win32k"] == "block_fwd"
+
+
+@pytest.mark.parametrize("name", ["traffic_block_fwd_win32k.json", "traffic_block_bwd_bwd16k.json",
+                                  "traffic_merge_hbm_16k.json"])
+def test_committed_traffic_matches_the_kernel_sources(name):
+    """The HBM bytes committed for the headline kernel, the staged backward and the merge were
+    counted on the sources as they stand: a kernel edited since then needs its counters taken
+    again (the bench line would otherwise report no traffic)."""
+    import bench
+    t = json.load(open(os.path.join(ROOT, "profiles", name)))
+    assert t["source_hash"] == bench.kernel_source_hash(t["kernel"]), name
+    assert t["bytes_per_launch"] > 0
