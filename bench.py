@@ -32,7 +32,7 @@ Helper modes serve the measured HBM traffic:
                  flushed before each launch, then the same calibration copy;
   --traffic-from FETCH_CSV WRITE_CSV
                  turns the two counter-collection CSVs into a traffic file
-                 (profiles/traffic.json, or --traffic PATH): the kernel's KiB per
+                 (profiles/traffic_<kernel>_<workload>.json, or --traffic PATH): the kernel's KiB per
                  dispatch, each counter scaled by the bytes the copy moves over
                  what that counter read for it.
 """
@@ -91,8 +91,9 @@ def parse():
     ap.add_argument("--recompute-bwd", action="store_true",
                     help="at D = 128, the block backward without dS staging (the dQ kernel forms S and dP "
                          "again)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="measured HBM traffic per launch of the dominant kernel (from rocprofv3 --pmc)")
+    ap.add_argument("--traffic", default=None,
+                    help="where --traffic-from writes the measured HBM traffic per launch of the dominant "
+                         "kernel (default profiles/traffic_<kernel>_<workload>.json)")
     return ap.parse_args()
 
 
@@ -731,7 +732,7 @@ def traffic_from(args):
                     "bytes_per_launch": per_launch_kib * 1024.0 * factor}
         total += per_launch_kib * 1024.0 * factor
     out["bytes_per_launch"] = total
-    path = args.traffic
+    path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{name}_{out['workload']}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out))

@@ -110,9 +110,9 @@ def test_headline_is_the_32k_window_forward():
 
 
 @pytest.mark.parametrize("name", ["traffic_block_fwd_win32k.json", "traffic_block_bwd_bwd16k.json",
-                                  "traffic_merge_hbm_16k.json"])
+                                  "traffic_merge_hbm_16k.json", "traffic_block_bwd_gpt2s.json"])
 def test_committed_traffic_matches_the_kernel_sources(name):
-    """The HBM bytes committed for the headline kernel, the staged backward and the merge were
+    """The HBM bytes committed for the headline kernel, the backward kernels and the merge were
     counted on the sources as they stand: a kernel edited since then needs its counters taken
     again (the bench line would otherwise report no traffic)."""
     import bench
